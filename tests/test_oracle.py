@@ -1,0 +1,344 @@
+"""Pins of the CPU oracle against facts fixed outside it (CPU only).
+
+Each test ties one part of the oracle to something it does not compute
+itself: a hand-worked packing example, exhaustive round trips, exact
+arithmetic on tiny shapes, closed forms and special cases, and the
+effective-weight identity W_eff = W + g B A of the gated error compensator
+(SPEAR, gist.science summary, section 2.1 A).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_gemm_w4a16_amd import inputs as gen
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(bits):
+    return gen.bf16_to_f32(bits)
+
+
+def rand_bf16(rng, shape, sd=1.0):
+    return gen.bf16_bits(rng.normal(0, sd, size=shape).astype(np.float32))
+
+
+def rand_layer(rng, M, K, N, r, kind, hard=0, tau=0.0):
+    if kind == oracle.CODES_S4:
+        codes = rng.integers(-8, 8, size=(N, K), dtype=np.int8)
+        zeros = None
+    else:
+        codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+        zeros = rng.integers(0, 16, size=N, dtype=np.uint8)
+    packed, bad = oracle.pack_w4(codes, kind)
+    assert bad == 0
+    scales = rng.uniform(0.005, 0.02, size=N).astype(np.float32)
+    x = rand_bf16(rng, (M, K))
+    ec = {"A": rand_bf16(rng, (r, K), 0.02), "B": rand_bf16(rng, (N, r), 0.02),
+          "w_g": rand_bf16(rng, (K,), 1 / math.sqrt(K)), "b": 0.25, "tau": tau, "hard": hard}
+    return codes, packed, scales, zeros, x, ec
+
+
+# ------------------------------------------------------------------ packing
+
+def test_pack_worked_example():
+    g = json.load(open(os.path.join(GOLD, "pack_example.json")))
+    p, bad = oracle.pack_w4(np.array([g["s4"]["codes"]], dtype=np.int8), oracle.CODES_S4)
+    assert bad == 0 and p.tolist() == [g["s4"]["bytes"]]
+    assert oracle.unpack_w4(p, 8).tolist() == [g["s4"]["u"]]
+    p, bad = oracle.pack_w4(np.array([g["u4"]["codes"]], dtype=np.uint8), oracle.CODES_U4)
+    assert bad == 0 and p.tolist() == [g["u4"]["bytes"]]
+    # little-endian 32-bit view of the signed example
+    p, _ = oracle.pack_w4(np.array([g["s4"]["codes"]], dtype=np.int8), oracle.CODES_S4)
+    assert int(p.view("<u4")[0, 0]) == 0x3D5BF870
+
+
+@pytest.mark.parametrize("kind", [oracle.CODES_S4, oracle.CODES_U4])
+def test_pack_roundtrip_exhaustive(kind):
+    # every code value at every nibble position of a 32-code row
+    K = 32
+    base = np.zeros(K, dtype=np.int64)          # u = 0 everywhere else
+    rows = []
+    for pos in range(K):
+        for v in range(16):
+            row = base.copy()
+            row[pos] = v
+            rows.append(row)
+    u = np.array(rows, dtype=np.uint8)
+    codes = (u.astype(np.int16) - 8).astype(np.int8) if kind == oracle.CODES_S4 else u
+    p, bad = oracle.pack_w4(codes, kind)
+    assert bad == 0
+    assert np.array_equal(oracle.unpack_w4(p, K), u)
+    # the byte holding position pos carries v in the nibble the layout names
+    for i, (pos, v) in enumerate((pos, v) for pos in range(K) for v in range(16)):
+        byte = int(p[i, pos // 2])
+        other = 0
+        want = (v | (other << 4)) if pos % 2 == 0 else (other | (v << 4))
+        assert byte == want
+
+
+def test_unpack_all_bytes():
+    p = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    u = oracle.unpack_w4(p, 512)[0]
+    assert np.array_equal(u[0::2], np.arange(256) & 15)
+    assert np.array_equal(u[1::2], np.arange(256) >> 4)
+
+
+def test_pack_bad_codes_counted_and_masked():
+    c = np.array([[-9, 8, 7, -8, 0, 100, -128, 3]], dtype=np.int8)
+    p, bad = oracle.pack_w4(c, oracle.CODES_S4)
+    assert bad == 4
+    assert oracle.unpack_w4(p, 8).tolist() == [[(v + 8) & 15 for v in c[0].tolist()]]
+    c = np.array([[16, 15, 255, 0]], dtype=np.uint8)
+    p, bad = oracle.pack_w4(c, oracle.CODES_U4)
+    assert bad == 2
+    assert oracle.unpack_w4(p, 4).tolist() == [[0, 15, 15, 0]]
+
+
+def test_dequant_closed_form():
+    rng = np.random.default_rng(1)
+    N, K = 8, 64
+    u = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    z = rng.integers(0, 16, size=N, dtype=np.uint8)
+    p, _ = oracle.pack_w4(u, oracle.CODES_U4)
+    w = oracle.dequant_w4(p, np.ones(N, np.float32), z, K)
+    assert np.array_equal(w, u.astype(np.float32) - z[:, None])          # s = 1: exact ints
+    s = rng.uniform(0.005, 0.02, N).astype(np.float32)
+    w = oracle.dequant_w4(p, s, None, K)                                  # symmetric: z = 8
+    assert np.array_equal(w, s[:, None] * (u.astype(np.float32) - np.float32(8)))
+
+
+# --------------------------------------------------------------- main term
+
+def test_permutation_matrix_gives_exact_gather():
+    """s = 2^-e per channel, codes = z_n + P[n][k] for a non-involutive
+    permutation: y[m][n] = s_n * x[m][pi(n)] exactly.  A transposed weight,
+    a swapped nibble or a misindexed scale or zero point all fail here."""
+    rng = np.random.default_rng(2)
+    K = N = 64
+    pi = np.array([(i * 7 + 3) % K for i in range(N)])  # fixed, not an involution
+    assert any(pi[pi[i]] != i for i in range(N))
+    z = rng.integers(0, 15, size=N, dtype=np.uint8)
+    codes = np.repeat(z[:, None], K, axis=1).astype(np.uint8)
+    codes[np.arange(N), pi] += 1
+    p, _ = oracle.pack_w4(codes, oracle.CODES_U4)
+    s = (2.0 ** -rng.integers(0, 6, size=N)).astype(np.float32)
+    x = rand_bf16(rng, (5, K))
+    y = oracle.w4_linear(x, p, s, z)
+    assert np.array_equal(y, s[None, :].astype(np.float64) * f32(x)[:, pi].astype(np.float64))
+
+
+def test_integer_weights_match_library_matmul():
+    """s = 1, z = 0: W is an integer matrix and y = x W^T; numpy's fp64 matmul of
+    small integers times bf16 values is exact at K = 256."""
+    rng = np.random.default_rng(3)
+    M, K, N = 7, 256, 24
+    u = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    p, _ = oracle.pack_w4(u, oracle.CODES_U4)
+    x = gen.bf16_bits(rng.integers(-64, 64, size=(M, K)).astype(np.float32) / 8)
+    y = oracle.w4_linear(x, p, np.ones(N, np.float32), np.zeros(N, np.uint8))
+    assert np.array_equal(y, f32(x).astype(np.float64) @ u.astype(np.float64).T)
+
+
+@pytest.mark.parametrize("kind", [oracle.CODES_S4, oracle.CODES_U4])
+@pytest.mark.parametrize("hard", [0, 1])
+def test_tiny_exact_rational(kind, hard):
+    """Exact rational evaluation of the layer (including the gated EC) on tiny
+    shapes; the oracle must agree within fp64 rounding."""
+    rng = np.random.default_rng(10 + kind + 2 * hard)
+    M, K, N, r = 4, 32, 6, 4
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, kind, hard, tau=0.5)
+    y = oracle.w4_linear(x, p, s, z, ec)
+    gt = oracle.gate(x, ec["w_g"], ec["b"], ec["tau"], ec["hard"])
+    X = [[Fraction(float(v)) for v in row] for row in f32(x)]
+    u = codes.astype(np.int64) + (8 if kind == oracle.CODES_S4 else 0)
+    zz = np.full(N, 8) if z is None else z.astype(np.int64)
+    A = f32(ec["A"]).astype(np.float64)
+    B = f32(ec["B"]).astype(np.float64)
+    for m in range(M):
+        for n in range(N):
+            # the fp32 dequantised weight is exact here (s * small int, 24-bit s)
+            w = [Fraction(float(np.float32(s[n]) * np.float32(u[n, k] - zz[n]))) for k in range(K)]
+            y0 = sum(X[m][k] * w[k] for k in range(K))
+            exact = y0
+            if m in gt["idx"]:
+                e = sum(Fraction(float(B[n, j])) * sum(Fraction(float(A[j, k])) * X[m][k]
+                                                       for k in range(K)) for j in range(r))
+                exact += Fraction(float(gt["g"][m])) * e
+            scale = sum(abs(X[m][k] * w[k]) for k in range(K)) + 1
+            assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(1, 2 ** 45) * scale
+
+
+def test_higham_bound_c1_sample():
+    """At C1 size the fp64 result is within gamma_K * sum|x||w| of the correctly
+    rounded exact sum (math.fsum of exact products) on sampled outputs."""
+    d = gen.make(1)
+    p, _ = oracle.pack_w4(d["codes"], d["kind"])
+    rng = np.random.default_rng(4)
+    ms = rng.integers(0, d["M"], 64)
+    ns = rng.integers(0, d["N"], 64)
+    y = oracle.w4_linear_sampled(d["x"], p, d["scales"], d["zeros"], None, ms, ns)
+    w = oracle.dequant_w4(p, d["scales"], d["zeros"], d["K"]).astype(np.float64)
+    x = f32(d["x"]).astype(np.float64)
+    K = d["K"]
+    gam = K * 2.0 ** -53 / (1 - K * 2.0 ** -53)
+    for i, (m, n) in enumerate(zip(ms, ns)):
+        prods = x[m] * w[n]                      # exact: 8-bit x 24-bit mantissas
+        exact = math.fsum(prods)
+        assert abs(y[i] - exact) <= gam * np.sum(np.abs(prods)) + 1e-300
+
+
+# ---------------------------------------------------------------------- gate
+
+def test_gate_closed_forms():
+    K = 64
+    rng = np.random.default_rng(5)
+    wg = rand_bf16(rng, (K,), 0.3)
+    zero = np.zeros((3, K), np.uint16)
+    out = oracle.gate(zero, wg, 0.0, 0.5, 0)
+    assert np.all(out["z"] == 0.0) and np.all(out["g"] == np.float32(0.5))
+    out = oracle.gate(zero, wg, 1.75, 0.5, 0)
+    assert np.all(out["z"] == 1.75)
+    # one-hot tokens: z = b + w_g[k] exactly
+    eye = np.zeros((K, K), np.uint16)
+    eye[np.arange(K), np.arange(K)] = 0x3F80          # bf16 1.0
+    out = oracle.gate(eye, wg, -0.5, 0.5, 0)
+    assert np.array_equal(out["z"], f32(wg).astype(np.float64) - 0.5)
+    # sigmoid values: sigma(log 3) = 3/4, sigma(-z) = 1 - sigma(z), monotone
+    x = np.zeros((1, K), np.uint16)
+    for zval, want in [(math.log(3.0), 0.75), (0.0, 0.5), (-math.log(3.0), 0.25)]:
+        g = oracle.gate(x, wg, zval, 0.5, 0)["g"][0]
+        assert abs(float(g) - want) <= 2 ** -24
+    zs = np.linspace(-12, 12, 97)
+    gs = np.array([oracle.gate(x, wg, float(np.float32(zv)), 0.5, 0)["g"][0] for zv in zs])
+    assert np.all(np.diff(gs) >= 0)
+    assert np.allclose(gs + gs[::-1], 1.0, atol=2 ** -23)
+
+
+def test_selection_by_construction():
+    """Tokens c_m * e_k with w_g[k] = 1 have z_m = c_m exactly.  tau = 0.5 puts the
+    threshold at logit 0; ties skip."""
+    K = 32
+    wg = np.zeros(K, np.uint16)
+    wg[3] = 0x3F80
+    c = np.array([-2.0, 0.5, 3.0, 0.0, 1.0, -0.0, 2.0 ** -20], np.float32)
+    x = np.zeros((len(c), K), np.uint16)
+    x[:, 3] = gen.bf16_bits(c)
+    out = oracle.gate(x, wg, 0.0, 0.5, 1)
+    assert out["idx"].tolist() == [1, 2, 4, 6] and out["n_active"] == 4
+    assert oracle.gate(x, wg, 0.0, 1.0, 1)["n_active"] == 0          # tau = 1: none
+    assert oracle.gate(x, wg, 0.0, 0.0, 1)["idx"].tolist() == list(range(len(c)))  # tau = 0
+    assert oracle.gate(x, wg, 0.0, 0.9, 0)["idx"].tolist() == list(range(len(c)))  # soft
+    assert oracle.logit_threshold(0.5) == 0.0
+    assert oracle.logit_threshold(1.0) == math.inf
+    assert oracle.logit_threshold(0.0) == -math.inf
+    assert abs(oracle.logit_threshold(0.75) - math.log(3.0)) < 1e-15
+
+
+def test_selection_ascending_and_counts():
+    rng = np.random.default_rng(6)
+    M, K = 300, 128
+    x = rand_bf16(rng, (M, K))
+    wg = rand_bf16(rng, (K,), 1 / math.sqrt(K))
+    for tau in [0.1, 0.3, 0.5, 0.77]:
+        out = oracle.gate(x, wg, 0.0, tau, 1)
+        t = math.log(tau / (1 - tau))
+        idx = out["idx"]
+        assert np.all(np.diff(idx) > 0)
+        assert out["n_active"] == len(idx)
+        skipped = np.setdiff1d(np.arange(M), idx)
+        assert np.all(out["z"][idx] > oracle.logit_threshold(tau))
+        assert np.all(out["z"][skipped] <= oracle.logit_threshold(tau))
+        assert abs(oracle.logit_threshold(tau) - t) < 1e-6
+
+
+# ------------------------------------------------------- error compensator
+
+@pytest.mark.parametrize("hard", [0, 1])
+def test_effective_weight_identity(hard):
+    """Dense per-token effective weight W + g_m B A (the summary's W + alpha B
+    diag(gamma) A with a scalar gate, alpha = 1) applied to x[m] equals the
+    factored layer."""
+    rng = np.random.default_rng(7 + hard)
+    M, K, N, r = 6, 96, 40, 8
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_U4, hard, tau=0.5)
+    y = oracle.w4_linear(x, p, s, z, ec)
+    W = oracle.dequant_w4(p, s, z, K).astype(np.float64)                # [N][K]
+    A = f32(ec["A"]).astype(np.float64)                                  # [r][K]
+    B = f32(ec["B"]).astype(np.float64)                                  # [N][r]
+    gt = oracle.gate(x, ec["w_g"], ec["b"], ec["tau"], ec["hard"])
+    X = f32(x).astype(np.float64)
+    for m in range(M):
+        gm = float(gt["g"][m]) if m in gt["idx"] else 0.0
+        Weff = W + gm * (B @ A)
+        np.testing.assert_allclose(y[m], Weff @ X[m], rtol=1e-12, atol=1e-12)
+    if hard:
+        assert 0 < gt["n_active"] < M
+
+
+def test_rank1_closed_form():
+    """A = a e_k0^T, B = b c^T: the EC term is g_m x[m][k0] b_n (c . a)."""
+    rng = np.random.default_rng(8)
+    M, K, N, r = 5, 64, 12, 4
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_S4)
+    k0 = 17
+    a = np.array([0.5, -0.25, 1.0, 2.0], np.float32)
+    cvec = np.array([1.0, 0.5, -1.0, 0.25], np.float32)
+    bvec = (rng.integers(-8, 8, N) / 16).astype(np.float32)
+    A = np.zeros((r, K), np.float32)
+    A[:, k0] = a
+    ec["A"] = gen.bf16_bits(A)
+    ec["B"] = gen.bf16_bits(np.outer(bvec, cvec))
+    y = oracle.w4_linear(x, p, s, z, ec)
+    y0 = oracle.w4_linear(x, p, s, z, None)
+    g = oracle.gate(x, ec["w_g"], ec["b"], 0.0, 0)["g"].astype(np.float64)
+    X = f32(x).astype(np.float64)
+    want = g[:, None] * X[:, k0:k0 + 1] * bvec[None, :] * float(np.dot(cvec, a))
+    np.testing.assert_allclose(y - y0, want, rtol=1e-12, atol=1e-14)
+
+
+def test_reductions_to_plain_w4():
+    rng = np.random.default_rng(9)
+    M, K, N, r = 6, 64, 16, 8
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_U4)
+    plain = oracle.w4_linear(x, p, s, z, None)
+    e = dict(ec, A=np.zeros_like(ec["A"]))                   # A = 0
+    assert np.array_equal(oracle.w4_linear(x, p, s, z, e), plain)
+    e = dict(ec, b=-math.inf)                                # g = 0 (soft)
+    assert np.array_equal(oracle.w4_linear(x, p, s, z, e), plain)
+    e = dict(ec, hard=1, tau=1.0)                            # tau = 1: nobody
+    assert np.array_equal(oracle.w4_linear(x, p, s, z, e), plain)
+    e = dict(ec, hard=1, tau=0.0)                            # tau = 0 == soft
+    assert np.array_equal(oracle.w4_linear(x, p, s, z, e), oracle.w4_linear(x, p, s, z, ec))
+    assert not np.array_equal(oracle.w4_linear(x, p, s, z, ec), plain)
+
+
+def test_rows_independent_and_sampled_consistent():
+    rng = np.random.default_rng(11)
+    M, K, N, r = 9, 64, 20, 8
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_S4, 1, 0.45)
+    y = oracle.w4_linear(x, p, s, z, ec)
+    for m in [0, 4, 8]:
+        assert np.array_equal(oracle.w4_linear(x[m:m + 1], p, s, z, ec)[0], y[m])
+    ms = rng.integers(0, M, 40)
+    ns = rng.integers(0, N, 40)
+    assert np.array_equal(oracle.w4_linear_sampled(x, p, s, z, ec, ms, ns), y[ms, ns])
+
+
+def test_generator_workloads_shapes_and_rates():
+    d = gen.make(3)
+    assert d["x"].shape == (64, 4096) and d["codes"].shape == (14336, 4096)
+    assert len(d["outlier_channels"]) == 41 and d["ec"]["r"] == 64
+    out = oracle.gate(d["x"], d["ec"]["w_g"], d["ec"]["b"], d["ec"]["tau"], 1)
+    skip = 1 - out["n_active"] / 64
+    assert 0.2 < skip < 0.6
+    t = oracle.logit_threshold(d["ec"]["tau"])
+    assert np.min(np.abs(out["z"] - t)) > 1e-9
+    for cfg in (1, 2, 4):
+        d = gen.make(cfg)
+        assert d["codes"].shape == (d["N"], d["K"])
