@@ -1,0 +1,195 @@
+/*
+ * spear.h -- C ABI of libspear: a W4A16 linear layer with a per-token gated
+ * Error Compensator (EC), written for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page title, then section):
+ *   "SPEAR: A System for Post-Quantization Error-Adaptive Recovery Enabling
+ *   Efficient Low-Bit LLM Serving"
+ *     - authors' abstract (fugumt.com record of arXiv 2606.11244): 4-bit
+ *       per-channel weights, ECs modulated by per-token gates, the EC fused
+ *       into the low-bit GEMM;
+ *     - gist.science technical summary, section 2.1 A: the EC maps x to rank r
+ *       with A, gates it per token, maps back with B; the effective weight is
+ *       W + alpha B diag(gamma) A;
+ *     - same summary, section 2.2 A: phase-aware dispatch -- at decode the EC
+ *       is fused into the GEMM epilogue (one kernel), at prefill it runs
+ *       semi-fused;
+ *     - same summary, section 3.1: per-channel 4-bit quantizers (RTN, GPTQ,
+ *       AWQ, OmniQuant) -- the layer takes their codes as given.
+ *
+ * Computation (all shapes row-major; tokens are rows):
+ *   x     [M][K]  bf16 activations
+ *   W     [N][K]  4-bit codes u (packed, see spear_pack_w4), per-output-channel
+ *                 scale s[N] (fp32) and zero point z[N] (uint8; 8 when NULL)
+ *   A     [r][K]  bf16 EC down-projection
+ *   B     [N][r]  bf16 EC up-projection (alpha folded in)
+ *   w_g   [K]     bf16 gate weights, b fp32 gate bias
+ *
+ *   z_m   = b + sum_k x[m][k] w_g[k]                  (gate logit, fp64 sum)
+ *   g_m   = 1 / (1 + exp(-z_m))                       (fp32)
+ *   act_m = hard ? (z_m > log(tau / (1 - tau))) : 1   (a tie skips)
+ *   y[m][n] = s_n sum_k x[m][k] (u[n][k] - z_n)
+ *           + act_m g_m sum_j B[n][j] sum_k A[j][k] x[m][k]
+ *
+ * Conventions shared by every entry point:
+ *   - Data pointers are DEVICE pointers unless stated otherwise.  The caller
+ *     allocates and owns all memory, including the workspace.  The library
+ *     never allocates device memory and keeps no per-call state.
+ *   - Every call enqueues work on `stream` (a hipStream_t; NULL is the null
+ *     stream) and returns without synchronising.  Faults inside a kernel
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before any HIP call.  A call that
+ *     returns an error has enqueued nothing.
+ *   - All functions are thread-safe.  A workspace must not be shared by calls
+ *     that may run concurrently (for example on two streams).
+ */
+#ifndef SPEAR_H
+#define SPEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEAR_ABI_VERSION 1
+
+typedef uint16_t spear_bf16; /* raw bfloat16 bits */
+typedef int32_t spear_status;
+
+#define SPEAR_OK            0
+#define SPEAR_E_NULL       -1 /* a required pointer is NULL                      */
+#define SPEAR_E_SHAPE      -2 /* a size is out of range (see each entry point)   */
+#define SPEAR_E_ALIGN      -3 /* a pointer is not aligned as required            */
+#define SPEAR_E_ARG        -4 /* an enum is out of range or tau is NaN           */
+#define SPEAR_E_WORKSPACE  -5 /* workspace smaller than spear_w4_linear_workspace_size */
+#define SPEAR_E_HIP        -6 /* a HIP runtime call or kernel launch failed      */
+#define SPEAR_E_DEVICE     -7 /* the current device is not gfx950                */
+
+/* Code kinds accepted by spear_pack_w4. */
+#define SPEAR_CODES_S4 0 /* int8 codes q in [-8, 7]; stored offset-binary u = q + 8, zero point 8 */
+#define SPEAR_CODES_U4 1 /* uint8 codes u in [0, 15]; zero point per channel */
+
+/* Output element types of spear_w4_linear. */
+#define SPEAR_OUT_BF16 0 /* y rounded to bf16 (round to nearest even) */
+#define SPEAR_OUT_F32  1 /* y in fp32 */
+
+/* Kernel-path selection of spear_w4_linear_path. */
+#define SPEAR_PATH_AUTO          0 /* decode path for M <= 16, prefill path otherwise   */
+#define SPEAR_PATH_DECODE        1 /* M <= 16: one launch, EC fused into the epilogue   */
+#define SPEAR_PATH_PREFILL       2 /* any M: EC pre-pass, then the MFMA GEMM whose
+                                      epilogue applies the EC                           */
+#define SPEAR_PATH_DECODE_2PASS  3 /* M <= 16: EC pre-pass, then the decode kernel      */
+
+/* Largest EC rank accepted; the rank must also be a multiple of 8. */
+#define SPEAR_MAX_RANK 256
+
+/* Quantised weights (all device pointers). */
+typedef struct spear_w4 {
+    const uint8_t *packed; /* [N][K/2] from spear_pack_w4; 16-byte aligned          */
+    const float *scales;   /* [N] per-channel scale s_n; 4-byte aligned              */
+    const uint8_t *zeros;  /* [N] zero points in [0, 15], or NULL for zero point 8   */
+    int64_t N;             /* output channels, >= 1                                   */
+    int64_t K;             /* input channels, >= 32 and a multiple of 32              */
+} spear_w4;
+
+/* Error compensator and gate (device pointers; the *_out fields are optional). */
+typedef struct spear_ec {
+    const spear_bf16 *A;      /* [r][K]; 16-byte aligned                            */
+    const spear_bf16 *B;      /* [N][r]; 16-byte aligned                            */
+    const spear_bf16 *w_gate; /* [K]; 16-byte aligned                               */
+    float b;                  /* gate bias (-inf gives g = 0)                       */
+    float tau;                /* hard-gate threshold on g; must not be NaN          */
+    int32_t hard;             /* 0: every token takes the EC; 1: only z_m > logit(tau) */
+    int32_t r;                /* rank, a multiple of 8 in [8, SPEAR_MAX_RANK]       */
+    float *g_out;             /* optional [M]: g_m                                  */
+    int32_t *idx_out;         /* optional [M]: ascending indices of active tokens   */
+    int32_t *n_active_out;    /* optional [1]: number of active tokens              */
+} spear_ec;
+
+/*
+ * spear_pack_w4 -- pack 4-bit codes for spear_w4_linear.
+ *   codes     [N][K] int8 (SPEAR_CODES_S4) or uint8 (SPEAR_CODES_U4); 16-byte aligned.
+ *   packed    [N][K/2] output; byte [n][i] holds u[n][2i] in bits 0-3 and
+ *             u[n][2i+1] in bits 4-7 (u = q + 8 for signed codes).  16-byte aligned.
+ *   bad_codes optional device int32 counter; the number of out-of-range codes is
+ *             ADDED to it.  Out-of-range codes are packed as their low 4 bits.
+ * Shapes: N >= 1, K >= 32, K % 32 == 0.  Source: the summary's section 3.1
+ * (per-channel 4-bit codes from any quantizer); the layout is this library's.
+ */
+spear_status spear_pack_w4(const void *codes, int32_t code_kind, int64_t N, int64_t K,
+                           uint8_t *packed, int32_t *bad_codes, void *stream);
+
+/*
+ * spear_gate -- the per-token gate and hard-gate token selection alone.
+ *   x [M][K] bf16 (16-byte aligned), w_gate [K] bf16 (16-byte aligned).
+ *   g        [M] fp32 output, g_m = sigmoid(z_m).
+ *   idx      [M] int32 output; entries [0, n_active) are the active tokens in
+ *            ascending order, the rest are left unspecified.
+ *   n_active [1] int32 output.
+ * Shapes: M >= 0 (M == 0 writes n_active = 0), K >= 32, K % 32 == 0.
+ * Sources: abstract (per-token gates); summary section 2.1 A (input-dependent gate).
+ */
+spear_status spear_gate(const spear_bf16 *x, int64_t M, int64_t K, const spear_bf16 *w_gate,
+                        float b, float tau, int32_t hard, float *g, int32_t *idx,
+                        int32_t *n_active, void *stream);
+
+/*
+ * spear_w4_linear_workspace_size -- bytes of workspace spear_w4_linear needs
+ * for these sizes (r = 0 when there is no EC).  Host-only, no HIP call.
+ */
+size_t spear_w4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r);
+
+/*
+ * spear_workspace_init -- zero a workspace before its first use (a workspace
+ * allocated zero-filled needs no init).  The kernels leave it in that state.
+ * ws: device pointer, 256-byte aligned; bytes >= 256.
+ */
+spear_status spear_workspace_init(void *ws, size_t bytes, void *stream);
+
+/*
+ * spear_w4_linear -- y = x W^T (dequantised) + gated EC; ec == NULL gives the
+ * plain W4 linear.  Sources: abstract; summary sections 2.1 A and 2.2 A.
+ *   x         [M][K] bf16, 16-byte aligned.  M >= 0 (M == 0 does nothing but
+ *             write *n_active_out = 0 when that pointer is given).
+ *   w         weights; w->N >= 1, w->K >= 32, w->K % 32 == 0.
+ *   ec        EC and gate, or NULL.
+ *   y         [M][N] output, fp32 or bf16 per out_dtype; 16-byte aligned.
+ *   workspace device scratch of at least spear_w4_linear_workspace_size bytes,
+ *             256-byte aligned, zeroed once (see spear_workspace_init).
+ * Dispatch: M <= 16 takes the decode path (one launch; the gate, token
+ * selection and EC down-projection run in the same kernel as the weight
+ * stream, and the EC is applied in its epilogue); M > 16 takes the prefill
+ * path (an EC pre-pass, then the MFMA GEMM with the EC in its epilogue).
+ * The result does not depend on the path beyond fp32 rounding order.
+ */
+spear_status spear_w4_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                             const spear_ec *ec, void *y, int32_t out_dtype,
+                             void *workspace, size_t ws_bytes, void *stream);
+
+/* spear_w4_linear with an explicit SPEAR_PATH_* (the decode paths need M <= 16). */
+spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                  const spear_ec *ec, void *y, int32_t out_dtype,
+                                  void *workspace, size_t ws_bytes, int32_t path,
+                                  void *stream);
+
+/*
+ * The fused decode kernel's epilogue waits (bounded) for the EC vector that
+ * other workgroups of the same launch produce.  If a wait exceeds the limit
+ * the affected outputs are written without the EC and a counter in the
+ * workspace is incremented.  spear_set_wait_limit sets the limit in polling
+ * rounds for later launches (0 restores the default, about a second);
+ * spear_workspace_timeouts synchronises `stream`, copies the counter to
+ * *host_count and clears it.
+ */
+void spear_set_wait_limit(uint32_t rounds);
+spear_status spear_workspace_timeouts(void *workspace, int32_t *host_count, void *stream);
+
+const char *spear_status_string(spear_status s);
+int32_t spear_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEAR_H */

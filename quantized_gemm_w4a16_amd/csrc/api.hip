@@ -1,0 +1,331 @@
+// api.hip -- host side of libspear: argument validation, workspace layout and
+// phase-aware dispatch (decode vs prefill) for gfx950.
+//
+// Source for the dispatch: "SPEAR: A System for Post-Quantization
+// Error-Adaptive Recovery Enabling Efficient Low-Bit LLM Serving",
+// gist.science summary section 2.2 A (decode: EC fused into the low-bit GEMM
+// epilogue; prefill: EC semi-fused).
+#include <math.h>
+#include <mutex>
+#include <string.h>
+
+#include "spear_internal.hpp"
+
+namespace spear {
+
+static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
+{
+    WsLayout L;
+    memset(&L, 0, sizeof L);
+    const bool decode = M <= 16;
+    L.ncg = cdiv(N, 16);
+    const int64_t S = cdiv(K, 128);
+    L.ksplit = cdiv(S, DEC_SPW);
+    L.rpad = r > 0 ? cdiv(r, 32) * 32 : 0;
+    L.mpad = cdiv(M > 0 ? M : 1, 16) * 16;
+    int64_t nprod = cdiv(K, PROD_K);
+    const int64_t nwg = L.ncg * L.ksplit;
+    if (nprod > nwg)
+        nprod = nwg;
+    if (nprod > MAX_PROD)
+        nprod = MAX_PROD;
+    L.prod_k = cdiv(cdiv(K, nprod), 32) * 32;
+    L.nprod = cdiv(K, L.prod_k);
+
+    size_t off = 0;
+    L.hdr = off;
+    off = align256(off + HDR_WORDS * sizeof(uint32_t));
+    L.colcnt = off;
+    off = align256(off + (size_t)L.ncg * sizeof(uint32_t));
+    L.splitp = off;
+    if (decode && L.ksplit > 1)
+        off = align256(off + (size_t)(L.ncg * L.ksplit * 64 * 5) * sizeof(float));
+    L.produ = off;
+    L.prodz = off;
+    if (decode && r > 0) {
+        off = align256(off + (size_t)(L.nprod * 16 * L.rpad) * sizeof(float));
+        L.prodz = off;
+        off = align256(off + (size_t)(L.nprod * 16) * sizeof(double));
+    }
+    L.vhi = L.vlo = L.active = off;
+    if (r > 0) {
+        L.vhi = off;
+        off = align256(off + (size_t)(L.mpad * L.rpad) * 2);
+        L.vlo = off;
+        off = align256(off + (size_t)(L.mpad * L.rpad) * 2);
+        L.active = off;
+        off = align256(off + (size_t)L.mpad * 4);
+    }
+    L.total = off;
+    return L;
+}
+
+static uint32_t g_wait_limit = 0;
+static const uint32_t DEFAULT_WAIT_LIMIT = 1u << 20;
+
+// gfx950 check, cached per device.
+static spear_status check_device()
+{
+    static std::mutex mu;
+    static int known[64];   // 0 unknown, 1 ok, 2 not gfx950
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return SPEAR_E_HIP;
+    if (dev < 0 || dev >= 64)
+        return SPEAR_E_DEVICE;
+    std::lock_guard<std::mutex> lk(mu);
+    if (known[dev] == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess)
+            return SPEAR_E_HIP;
+        known[dev] = strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    }
+    return known[dev] == 1 ? SPEAR_OK : SPEAR_E_DEVICE;
+}
+
+static bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+static double logit_threshold(float tau)
+{
+    const double t = (double)tau;
+    if (t >= 1.0)
+        return INFINITY;
+    if (t <= 0.0)
+        return -INFINITY;
+    return log(t / (1.0 - t));
+}
+
+static spear_status hip_status(hipError_t e) { return e == hipSuccess ? SPEAR_OK : SPEAR_E_HIP; }
+
+static const int64_t GRID_MAX = 0x7FFFFFFF;
+
+} // namespace spear
+
+using namespace spear;
+
+extern "C" {
+
+int32_t spear_abi_version(void) { return SPEAR_ABI_VERSION; }
+
+const char *spear_status_string(spear_status s)
+{
+    switch (s) {
+    case SPEAR_OK: return "ok";
+    case SPEAR_E_NULL: return "a required pointer is NULL";
+    case SPEAR_E_SHAPE: return "a size is out of range";
+    case SPEAR_E_ALIGN: return "a pointer is not aligned as required";
+    case SPEAR_E_ARG: return "an argument value is invalid";
+    case SPEAR_E_WORKSPACE: return "workspace too small";
+    case SPEAR_E_HIP: return "HIP runtime error";
+    case SPEAR_E_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+    }
+}
+
+void spear_set_wait_limit(uint32_t rounds) { g_wait_limit = rounds; }
+
+spear_status spear_pack_w4(const void *codes, int32_t code_kind, int64_t N, int64_t K,
+                           uint8_t *packed, int32_t *bad_codes, void *stream)
+{
+    if (!codes || !packed)
+        return SPEAR_E_NULL;
+    if (N < 1 || K < 32 || K % 32 != 0 || N > ((int64_t)1 << 40) / K)
+        return SPEAR_E_SHAPE;
+    if (code_kind != SPEAR_CODES_S4 && code_kind != SPEAR_CODES_U4)
+        return SPEAR_E_ARG;
+    if (!aligned(codes, 16) || !aligned(packed, 16) || !aligned(bad_codes, 4))
+        return SPEAR_E_ALIGN;
+    if (cdiv(N * K / 16, 256) > GRID_MAX)
+        return SPEAR_E_SHAPE;
+    spear_status st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    return hip_status(launch_pack(codes, code_kind, N, K, packed, bad_codes, (hipStream_t)stream));
+}
+
+spear_status spear_gate(const spear_bf16 *x, int64_t M, int64_t K, const spear_bf16 *w_gate,
+                        float b, float tau, int32_t hard, float *g, int32_t *idx,
+                        int32_t *n_active, void *stream)
+{
+    if (!w_gate || !n_active || (M > 0 && (!x || !g || !idx)))
+        return SPEAR_E_NULL;
+    if (M < 0 || K < 32 || K % 32 != 0 || cdiv(M, 4) > GRID_MAX)
+        return SPEAR_E_SHAPE;
+    if (isnan(tau) || isnan(b) || (hard != 0 && hard != 1))
+        return SPEAR_E_ARG;
+    if (!aligned(x, 16) || !aligned(w_gate, 16) || !aligned(g, 4) || !aligned(idx, 4) ||
+        !aligned(n_active, 4))
+        return SPEAR_E_ALIGN;
+    spear_status st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    return hip_status(launch_gate(x, M, K, w_gate, b, logit_threshold(tau), hard, g, idx,
+                                  n_active, (hipStream_t)stream));
+}
+
+size_t spear_w4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r)
+{
+    if (M < 0 || N < 1 || K < 32 || r < 0)
+        return 0;
+    return ws_layout(M, N, K, r).total;
+}
+
+spear_status spear_workspace_init(void *ws, size_t bytes, void *stream)
+{
+    if (!ws)
+        return SPEAR_E_NULL;
+    if (bytes < 256)
+        return SPEAR_E_WORKSPACE;
+    if (!aligned(ws, 256))
+        return SPEAR_E_ALIGN;
+    spear_status st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    return hip_status(launch_zero(ws, bytes, (hipStream_t)stream));
+}
+
+spear_status spear_workspace_timeouts(void *workspace, int32_t *host_count, void *stream)
+{
+    if (!workspace || !host_count)
+        return SPEAR_E_NULL;
+    if (!aligned(workspace, 256))
+        return SPEAR_E_ALIGN;
+    spear_status st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t *cnt = reinterpret_cast<uint32_t *>(workspace) + HDR_TIMEOUTS;
+    uint32_t v = 0;
+    if (hipMemcpyAsync(&v, cnt, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess)
+        return SPEAR_E_HIP;
+    if (launch_zero(cnt, sizeof v, s) != hipSuccess)
+        return SPEAR_E_HIP;
+    if (hipStreamSynchronize(s) != hipSuccess)
+        return SPEAR_E_HIP;
+    *host_count = (int32_t)v;
+    return SPEAR_OK;
+}
+
+spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                  const spear_ec *ec, void *y, int32_t out_dtype,
+                                  void *workspace, size_t ws_bytes, int32_t path, void *stream)
+{
+    // ---- validation (no HIP call before it passes)
+    if (!w || !workspace || !w->packed || !w->scales)
+        return SPEAR_E_NULL;
+    if (M > 0 && (!x || !y))
+        return SPEAR_E_NULL;
+    if (ec && (!ec->A || !ec->B || !ec->w_gate))
+        return SPEAR_E_NULL;
+    const int64_t N = w->N, K = w->K;
+    if (M < 0 || N < 1 || K < 32 || K % 32 != 0)
+        return SPEAR_E_SHAPE;
+    if (ec && (ec->r < 8 || ec->r > SPEAR_MAX_RANK || ec->r % 8 != 0))
+        return SPEAR_E_SHAPE;
+    if (path < SPEAR_PATH_AUTO || path > SPEAR_PATH_DECODE_2PASS)
+        return SPEAR_E_ARG;
+    if (out_dtype != SPEAR_OUT_BF16 && out_dtype != SPEAR_OUT_F32)
+        return SPEAR_E_ARG;
+    if (ec && (isnan(ec->tau) || isnan(ec->b) || (ec->hard != 0 && ec->hard != 1)))
+        return SPEAR_E_ARG;
+    if (path == SPEAR_PATH_AUTO)
+        path = M <= 16 ? SPEAR_PATH_DECODE : SPEAR_PATH_PREFILL;
+    if ((path == SPEAR_PATH_DECODE || path == SPEAR_PATH_DECODE_2PASS) && M > 16)
+        return SPEAR_E_SHAPE;
+    if (!aligned(x, 16) || !aligned(w->packed, 16) || !aligned(w->scales, 4) ||
+        !aligned(y, 16) || !aligned(workspace, 256))
+        return SPEAR_E_ALIGN;
+    if (ec && (!aligned(ec->A, 16) || !aligned(ec->B, 16) || !aligned(ec->w_gate, 16) ||
+               !aligned(ec->g_out, 4) || !aligned(ec->idx_out, 4) ||
+               !aligned(ec->n_active_out, 4)))
+        return SPEAR_E_ALIGN;
+    const int32_t r = ec ? ec->r : 0;
+    const WsLayout L = ws_layout(M, N, K, r);
+    if (ws_bytes < L.total)
+        return SPEAR_E_WORKSPACE;
+    if (L.ncg * L.ksplit > GRID_MAX || cdiv(N, 64) * cdiv(M, 64) > GRID_MAX)
+        return SPEAR_E_SHAPE;
+    spear_status st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (M == 0) {
+        if (ec && ec->n_active_out)
+            return hip_status(launch_zero(ec->n_active_out, sizeof(int32_t), s));
+        return SPEAR_OK;
+    }
+
+    LinearArgs a;
+    memset(&a, 0, sizeof a);
+    a.x = x;
+    a.packed = w->packed;
+    a.scales = w->scales;
+    a.zeros = w->zeros;
+    a.y = y;
+    a.ws = reinterpret_cast<uint8_t *>(workspace);
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.ncg = L.ncg;
+    a.ksplit = L.ksplit;
+    a.nprod = L.nprod;
+    a.prod_k = L.prod_k;
+    a.mpad = L.mpad;
+    a.L = L;
+    a.out_f32 = out_dtype == SPEAR_OUT_F32;
+    a.wait_limit = g_wait_limit ? g_wait_limit : DEFAULT_WAIT_LIMIT;
+    if (ec) {
+        a.A = ec->A;
+        a.B = ec->B;
+        a.wg = ec->w_gate;
+        a.b = ec->b;
+        a.thr = logit_threshold(ec->tau);
+        a.hard = ec->hard;
+        a.r = ec->r;
+        a.rpad = (int32_t)L.rpad;
+        a.g_out = ec->g_out;
+        a.idx_out = ec->idx_out;
+        a.nact_out = ec->n_active_out;
+    }
+
+    hipError_t e = hipSuccess;
+    const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + L.active);
+    switch (path) {
+    case SPEAR_PATH_DECODE:
+        e = launch_decode(a, ec ? 1 : 0, s);
+        break;
+    case SPEAR_PATH_DECODE_2PASS:
+        if (ec) {
+            e = launch_prepass(a, s);
+            if (e == hipSuccess && (a.idx_out || a.nact_out))
+                e = launch_compact(active, M, a.idx_out, a.nact_out, s);
+        }
+        if (e == hipSuccess)
+            e = launch_decode(a, ec ? 2 : 0, s);
+        break;
+    default:
+        if (ec) {
+            e = launch_prepass(a, s);
+            if (e == hipSuccess && (a.idx_out || a.nact_out))
+                e = launch_compact(active, M, a.idx_out, a.nact_out, s);
+        }
+        if (e == hipSuccess)
+            e = launch_gemm(a, ec ? 1 : 0, s);
+        break;
+    }
+    return hip_status(e);
+}
+
+spear_status spear_w4_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                             const spear_ec *ec, void *y, int32_t out_dtype, void *workspace,
+                             size_t ws_bytes, void *stream)
+{
+    return spear_w4_linear_path(x, M, w, ec, y, out_dtype, workspace, ws_bytes,
+                                SPEAR_PATH_AUTO, stream);
+}
+
+} // extern "C"

@@ -1,0 +1,352 @@
+// prefill.hip -- prefill-sized W4A16 linear: the EC pre-pass and the MFMA GEMM
+// whose epilogue applies the gated error compensator (gfx950).
+//
+// Source: "SPEAR: A System for Post-Quantization Error-Adaptive Recovery
+// Enabling Efficient Low-Bit LLM Serving", gist.science summary section 2.2 A:
+// at prefill the layer is compute bound and the EC runs semi-fused -- here the
+// gate and the EC down-projection run in a short pre-pass and the
+// up-projection is folded into the GEMM epilogue.  The EC follows section
+// 2.1 A with the scalar gate g = sigmoid(b + x.w_g).
+#include "spear_internal.hpp"
+
+namespace spear {
+
+namespace {
+
+// --------------------------------------------------------------------- pre-pass
+// One workgroup per 16 tokens; its 4 waves split K.  Per token: gate logit in
+// fp64, g, hard-gate flag, u = A x (fp32 via MFMA, natural depth order on both
+// operands), v = g u (0 for skipped tokens) stored as bf16 hi + lo.
+__global__ __launch_bounds__(256) void prepass_kernel(const LinearArgs a)
+{
+    __shared__ f32x4 s_u[4][2][64];
+    __shared__ double s_z[4][64];
+    __shared__ float s_g[16];
+    __shared__ int s_act[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int64_t M = a.M, K = a.K;
+    const int64_t m0 = (int64_t)blockIdx.x * 16;
+    const int64_t T = K / 32, t0 = wave * T / 4, t1 = (wave + 1) * T / 4;
+    const int64_t m = m0 + lr;
+    const bool mv = m < M;
+    const int rpad = a.rpad, r = a.r;
+    uint16_t *vhi = reinterpret_cast<uint16_t *>(a.ws + a.L.vhi);
+    uint16_t *vlo = reinterpret_cast<uint16_t *>(a.ws + a.L.vlo);
+    int32_t *active = reinterpret_cast<int32_t *>(a.ws + a.L.active);
+
+    for (int jp = 0; jp < rpad / 32; jp++) {
+        f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+        double zp = 0.0;
+        const int j0 = 32 * jp + lr, j1 = j0 + 16;
+        for (int64_t t = t0; t < t1; t++) {
+            const int64_t k = 32 * t + 8 * lg;
+            const u32x4 xf = mv ? ld16(a.x + m * K + k) : zero4();
+            const u32x4 a0 = (j0 < r) ? ld16(a.A + (int64_t)j0 * K + k) : zero4();
+            const u32x4 a1 = (j1 < r) ? ld16(a.A + (int64_t)j1 * K + k) : zero4();
+            u0 = mfma16(a0, xf, u0);
+            u1 = mfma16(a1, xf, u1);
+            if (jp == 0) {
+                const u32x4 wv = ld16(a.wg + k);
+#pragma unroll
+                for (int e = 0; e < 4; e++) {
+                    zp += (double)(__uint_as_float(xf[e] << 16) * __uint_as_float(wv[e] << 16));
+                    zp += (double)(__uint_as_float(xf[e] & 0xFFFF0000u) *
+                                   __uint_as_float(wv[e] & 0xFFFF0000u));
+                }
+            }
+        }
+        s_u[wave][0][lane] = u0;
+        s_u[wave][1][lane] = u1;
+        if (jp == 0)
+            s_z[wave][lane] = zp;
+        __syncthreads();
+        if (jp == 0 && tid < 16) {
+            double z = (double)a.b;
+            for (int w = 0; w < 4; w++)
+                for (int q = 0; q < 4; q++)
+                    z += s_z[w][tid + 16 * q];
+            const int64_t mm = m0 + tid;
+            const float g = (float)(1.0 / (1.0 + exp(-z)));
+            const int act = (mm < M) && (a.hard ? (z > a.thr) : 1);
+            s_g[tid] = g;
+            s_act[tid] = act;
+            active[mm] = act;
+            if (mm < M && a.g_out)
+                a.g_out[mm] = g;
+        }
+        __syncthreads();
+        if (wave < 2) {
+            f32x4 u = {0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < 4; w++)
+                u += s_u[w][wave][lane];
+            // lane holds u[rank 32 jp + 16 wave + 4 lg + i][token m0 + lr]
+            const float g = s_act[lr] ? s_g[lr] : 0.f;
+            uint16_t hi[4], lo[4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const float v = g * u[i];
+                hi[i] = f2bf(v);
+                lo[i] = f2bf(v - bf16f(hi[i]));
+            }
+            const int64_t off = m * rpad + 32 * jp + 16 * wave + 4 * lg;
+            uint2 h, l;
+            h.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+            h.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+            l.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+            l.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+            *reinterpret_cast<uint2 *>(vhi + off) = h;
+            *reinterpret_cast<uint2 *>(vlo + off) = l;
+        }
+        __syncthreads();
+    }
+}
+
+// ------------------------------------------------------------------------ GEMM
+// Output tile BN channels x BM tokens, computed as W x^T so each lane ends with
+// 4 consecutive channels of one token (contiguous stores).  K advances in
+// 128-deep super-steps.  Packed weights: HBM -> registers (16-byte loads, one
+// super-step of prefetch), unpacked to bf16 128+u pairs in registers.
+// Activations: HBM -> registers -> LDS (double-buffered), permuted on the way
+// to match the unpacked pair order, and summed per token for the epilogue's
+// offset removal.  Epilogue: y = s_n (acc - (128 + z_n) sum_k x) + B v.
+template <int FN, int FM, int WNW, int WMW, int EC, int OUT_F32>
+__global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a)
+{
+    constexpr int NT = 64 * WNW * WMW;
+    constexpr int BN = 16 * FN * WNW, BM = 16 * FM * WMW;
+    constexpr int RS = 272;               // LDS bytes per token row: 16 chunks + pad
+    constexpr int CPT = BM * 16 / NT;     // 16-byte activation chunks per thread
+    static_assert((BM * 16) % NT == 0, "staging split");
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * RS];
+    __shared__ float s_rs[BM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int wn = wave % WNW, wm = wave / WNW;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
+    const int64_t ntiles = tiles_n * tiles_m;
+
+    // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
+    // of tiles (channels fastest) so its L2 shares activation rows and weights.
+    const int64_t bid = blockIdx.x;
+    const int64_t q8 = ntiles / 8, r8 = ntiles % 8;
+    const int64_t xcd = bid % 8, loc = bid / 8;
+    const int64_t tile = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
+    const int64_t n0 = (tile % tiles_n) * BN, m0 = (tile / tiles_n) * BM;
+    const int64_t S = (K + 127) / 128;
+
+    const int sc = tid & 15, srow0 = tid >> 4;
+    u32x4 xs[CPT];
+    float rsp[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; i++)
+        rsp[i] = 0.f;
+
+    u32x4 wc[FN], wx[FN];
+    f32x4 acc[FN][FM];
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++)
+            acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_w = [&](int64_t s, u32x4 *w) {
+        const int64_t k = 128 * s + 32 * lg;
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+            const int64_t nn = n0 + (wn * FN + fn) * 16 + lr;
+            w[fn] = (nn < N && k < K) ? ld16(a.packed + nn * (K / 2) + k / 2) : zero4();
+        }
+    };
+    auto load_x = [&](int64_t s) {
+        const int64_t k = 128 * s + 8 * sc;
+#pragma unroll
+        for (int i = 0; i < CPT; i++) {
+            const int64_t mm = m0 + srow0 + (NT / 16) * i;
+            xs[i] = (mm < M && k < K) ? ld16(a.x + mm * K + k) : zero4();
+        }
+    };
+    auto store_x = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < CPT; i++) {
+            const int row = srow0 + (NT / 16) * i;
+            rsp[i] = sum8(xs[i], rsp[i]);
+            *reinterpret_cast<u32x4 *>(&s_x[buf][row * RS + 16 * sc]) = perm8(xs[i]);
+        }
+    };
+
+    load_w(0, wc);
+    load_x(0);
+    store_x(0);
+    __syncthreads();
+    for (int64_t s = 0; s < S; s++) {
+        const int buf = (int)(s & 1);
+        const bool more = s + 1 < S;
+        if (more) {
+            load_w(s + 1, wx);
+            load_x(s + 1);
+        }
+        const uint8_t *xb = s_x[buf];
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+            u32x4 xf[FM];
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++) {
+                const int row = (wm * FM + fm) * 16 + lr;
+                xf[fm] = *reinterpret_cast<const u32x4 *>(xb + row * RS + (4 * lg + d) * 16);
+            }
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++) {
+                const u32x4 wa = unpack8(wc[fn][d]);
+#pragma unroll
+                for (int fm = 0; fm < FM; fm++)
+                    acc[fn][fm] = mfma16(wa, xf[fm], acc[fn][fm]);
+            }
+        }
+        if (more) {
+            store_x(buf ^ 1);
+#pragma unroll
+            for (int fn = 0; fn < FN; fn++)
+                wc[fn] = wx[fn];
+        }
+        __syncthreads();
+    }
+
+    // Per-token activation sums: 16 consecutive lanes share a row.
+#pragma unroll
+    for (int i = 0; i < CPT; i++) {
+        float v = rsp[i];
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        v += __shfl_xor(v, 4);
+        v += __shfl_xor(v, 8);
+        if (sc == 0)
+            s_rs[srow0 + (NT / 16) * i] = v;
+    }
+    __syncthreads();
+
+    // Epilogue.
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int64_t nn = n0 + (wn * FN + fn) * 16 + 4 * lg + i;
+            float sn = 0.f, zc = 0.f;
+            if (nn < N) {
+                sn = a.scales[nn];
+                zc = 128.f + (a.zeros ? (float)a.zeros[nn] : 8.f);
+            }
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++) {
+                const float rsm = s_rs[(wm * FM + fm) * 16 + lr];
+                acc[fn][fm][i] = sn * __builtin_fmaf(-zc, rsm, acc[fn][fm][i]);
+            }
+        }
+    }
+    if (EC) {
+        const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
+        const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
+        const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
+        int any = 0;
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) {
+            const int64_t mm = m0 + (wm * FM + fm) * 16 + lr;
+            any |= (mm < M) ? active[mm] : 0;
+        }
+        if (__ballot(any) != 0ull) {
+            const int rpad = a.rpad, r = a.r;
+            for (int t = 0; t < rpad / 32; t++) {
+                const int j = 32 * t + 8 * lg;
+                u32x4 vh[FM], vl[FM];
+#pragma unroll
+                for (int fm = 0; fm < FM; fm++) {
+                    const int64_t mm = m0 + (wm * FM + fm) * 16 + lr;
+                    vh[fm] = (mm < M) ? ld16(vhi + mm * rpad + j) : zero4();
+                    vl[fm] = (mm < M) ? ld16(vlo + mm * rpad + j) : zero4();
+                }
+#pragma unroll
+                for (int fn = 0; fn < FN; fn++) {
+                    const int64_t nn = n0 + (wn * FN + fn) * 16 + lr;
+                    const u32x4 bf = (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
+#pragma unroll
+                    for (int fm = 0; fm < FM; fm++) {
+                        acc[fn][fm] = mfma16(bf, vh[fm], acc[fn][fm]);
+                        acc[fn][fm] = mfma16(bf, vl[fm], acc[fn][fm]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+        const int64_t mm = m0 + (wm * FM + fm) * 16 + lr;
+        if (mm >= M)
+            continue;
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+            const int64_t nb = n0 + (wn * FN + fn) * 16 + 4 * lg;
+            const f32x4 v = acc[fn][fm];
+            if (OUT_F32) {
+                float *y = reinterpret_cast<float *>(a.y) + mm * N;
+                if (nb + 3 < N && (N & 3) == 0) {
+                    *reinterpret_cast<f32x4 *>(y + nb) = v;
+                } else {
+                    for (int i = 0; i < 4; i++)
+                        if (nb + i < N)
+                            y[nb + i] = v[i];
+                }
+            } else {
+                uint16_t *y = reinterpret_cast<uint16_t *>(a.y) + mm * N;
+                if (nb + 3 < N && (N & 3) == 0) {
+                    uint2 o;
+                    o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+                    o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+                    *reinterpret_cast<uint2 *>(y + nb) = o;
+                } else {
+                    for (int i = 0; i < 4; i++)
+                        if (nb + i < N)
+                            y[nb + i] = f2bf(v[i]);
+                }
+            }
+        }
+    }
+}
+
+template <int FN, int FM, int WNW, int WMW>
+hipError_t launch_gemm_t(const LinearArgs &a, int ec_on, hipStream_t s)
+{
+    constexpr int BN = 16 * FN * WNW, BM = 16 * FM * WMW;
+    const int64_t ntiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
+    const dim3 grid((unsigned)ntiles), block(64 * WNW * WMW);
+    if (ec_on) {
+        if (a.out_f32)
+            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 1, 1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 1, 0>), grid, block, 0, s, a);
+    } else {
+        if (a.out_f32)
+            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 0, 1>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 0, 0>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+} // namespace
+
+hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
+{
+    hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)((a.M + 15) / 16)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const LinearArgs &a, int ec_on, hipStream_t s)
+{
+    if (a.M <= 64)
+        return launch_gemm_t<2, 2, 2, 2>(a, ec_on, s);   // 64 x 64 tiles
+    return launch_gemm_t<4, 4, 2, 2>(a, ec_on, s);       // 128 x 128 tiles
+}
+
+} // namespace spear

@@ -1,0 +1,217 @@
+"""Thin ctypes binding of libspear (the C ABI declared in include/spear.h).
+
+Argument marshalling only: tensors are passed as device pointers together with
+torch's current HIP stream; every step of the layer runs in the library's
+kernels.  The library is opened on first use; if it has not been built the
+call raises (there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspear.so")
+
+SPEAR_OK = 0
+CODES_S4 = 0
+CODES_U4 = 1
+OUT_BF16 = 0
+OUT_F32 = 1
+PATH_AUTO = 0
+PATH_DECODE = 1
+PATH_PREFILL = 2
+PATH_DECODE_2PASS = 3
+MAX_RANK = 256
+
+EXPORTS = ("spear_pack_w4", "spear_gate", "spear_w4_linear_workspace_size",
+           "spear_workspace_init", "spear_w4_linear", "spear_w4_linear_path",
+           "spear_set_wait_limit", "spear_workspace_timeouts", "spear_status_string",
+           "spear_abi_version")
+
+
+class SpearError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+class _W4(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class _EC(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
+                ("b", ctypes.c_float), ("tau", ctypes.c_float), ("hard", ctypes.c_int32),
+                ("r", ctypes.c_int32), ("g_out", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
+                ("n_active_out", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load():
+    """Open libspear.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libspear.so not found at {LIB_PATH}; build it with "
+                           "quantized_gemm_w4a16_amd.build.build()")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    lib.spear_pack_w4.argtypes = [P, i32, i64, i64, P, P, P]
+    lib.spear_gate.argtypes = [P, i64, i64, P, ctypes.c_float, ctypes.c_float, i32, P, P, P, P]
+    lib.spear_w4_linear_workspace_size.argtypes = [i64, i64, i64, i32]
+    lib.spear_w4_linear_workspace_size.restype = ctypes.c_size_t
+    lib.spear_workspace_init.argtypes = [P, ctypes.c_size_t, P]
+    lin = [P, i64, ctypes.POINTER(_W4), ctypes.POINTER(_EC), P, i32, P, ctypes.c_size_t]
+    lib.spear_w4_linear.argtypes = lin + [P]
+    lib.spear_w4_linear_path.argtypes = lin + [i32, P]
+    lib.spear_set_wait_limit.argtypes = [ctypes.c_uint32]
+    lib.spear_set_wait_limit.restype = None
+    lib.spear_workspace_timeouts.argtypes = [P, ctypes.POINTER(i32), P]
+    lib.spear_status_string.argtypes = [i32]
+    lib.spear_status_string.restype = ctypes.c_char_p
+    lib.spear_abi_version.restype = i32
+    for name in ("spear_pack_w4", "spear_gate", "spear_workspace_init", "spear_w4_linear",
+                 "spear_w4_linear_path", "spear_workspace_timeouts"):
+        getattr(lib, name).restype = i32
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, st: int):
+    if st != SPEAR_OK:
+        raise SpearError(fn, st, load().spear_status_string(st).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+@dataclass
+class W4:
+    """Packed weights on the device: packed [N][K/2] uint8, scales [N] fp32,
+    zeros [N] uint8 or None (zero point 8)."""
+    packed: torch.Tensor
+    scales: torch.Tensor
+    zeros: Optional[torch.Tensor]
+    N: int
+    K: int
+
+    def _c(self):
+        return _W4(_ptr(self.packed), _ptr(self.scales), _ptr(self.zeros), self.N, self.K)
+
+
+@dataclass
+class EC:
+    """Error compensator on the device: A [r][K], B [N][r], w_gate [K] as bf16
+    (torch.bfloat16 or int16 bit tensors), gate bias b, threshold tau, hard flag.
+    Optional outputs g_out [M] fp32, idx_out [M] int32, n_active_out [1] int32."""
+    A: torch.Tensor
+    B: torch.Tensor
+    w_gate: torch.Tensor
+    b: float = 0.0
+    tau: float = 0.0
+    hard: int = 0
+    g_out: Optional[torch.Tensor] = None
+    idx_out: Optional[torch.Tensor] = None
+    n_active_out: Optional[torch.Tensor] = None
+
+    @property
+    def r(self) -> int:
+        return int(self.A.shape[0])
+
+    def _c(self):
+        return _EC(_ptr(self.A), _ptr(self.B), _ptr(self.w_gate), float(self.b), float(self.tau),
+                   int(self.hard), self.r, _ptr(self.g_out), _ptr(self.idx_out),
+                   _ptr(self.n_active_out))
+
+
+def spear_abi_version() -> int:
+    return int(load().spear_abi_version())
+
+
+def spear_status_string(st: int) -> str:
+    return load().spear_status_string(st).decode()
+
+
+def spear_pack_w4(codes: torch.Tensor, kind: int, packed: Optional[torch.Tensor] = None,
+                  bad_codes: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    N, K = codes.shape
+    if packed is None:
+        packed = torch.empty((N, K // 2), dtype=torch.uint8, device=codes.device)
+    _check("spear_pack_w4", load().spear_pack_w4(_ptr(codes), kind, N, K, _ptr(packed),
+                                                 _ptr(bad_codes), _stream(stream)))
+    return packed
+
+
+def spear_gate(x: torch.Tensor, w_gate: torch.Tensor, b: float, tau: float, hard: int,
+               g=None, idx=None, n_active=None, stream=None):
+    M, K = x.shape
+    dev = x.device
+    g = torch.empty(M, dtype=torch.float32, device=dev) if g is None else g
+    idx = torch.empty(max(M, 1), dtype=torch.int32, device=dev) if idx is None else idx
+    n_active = torch.empty(1, dtype=torch.int32, device=dev) if n_active is None else n_active
+    _check("spear_gate", load().spear_gate(_ptr(x), M, K, _ptr(w_gate), float(b), float(tau),
+                                           int(hard), _ptr(g), _ptr(idx), _ptr(n_active),
+                                           _stream(stream)))
+    return g, idx, n_active
+
+
+def spear_w4_linear_workspace_size(M: int, N: int, K: int, r: int) -> int:
+    return int(load().spear_w4_linear_workspace_size(M, N, K, r))
+
+
+def spear_workspace_init(ws: torch.Tensor, stream=None):
+    _check("spear_workspace_init", load().spear_workspace_init(_ptr(ws), ws.numel(),
+                                                               _stream(stream)))
+
+
+def new_workspace(M: int, N: int, K: int, r: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace tensor of the required size (torch allocation)."""
+    n = max(spear_w4_linear_workspace_size(M, N, K, r), 256)
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def spear_w4_linear(x: torch.Tensor, w: W4, ec: Optional[EC] = None,
+                    y: Optional[torch.Tensor] = None, out_dtype: int = OUT_F32,
+                    workspace: Optional[torch.Tensor] = None, path: int = PATH_AUTO,
+                    stream=None) -> torch.Tensor:
+    M = int(x.shape[0])
+    if y is None:
+        dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+        y = torch.empty((M, w.N), dtype=dt, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(M, w.N, w.K, ec.r if ec is not None else 0, x.device)
+    wc = w._c()
+    ecc = ec._c() if ec is not None else None
+    st = load().spear_w4_linear_path(_ptr(x), M, ctypes.byref(wc),
+                                     ctypes.byref(ecc) if ecc is not None else None,
+                                     _ptr(y), out_dtype, _ptr(workspace), workspace.numel(),
+                                     path, _stream(stream))
+    _check("spear_w4_linear", st)
+    return y
+
+
+def spear_set_wait_limit(rounds: int):
+    load().spear_set_wait_limit(int(rounds))
+
+
+def spear_workspace_timeouts(ws: torch.Tensor, stream=None) -> int:
+    out = ctypes.c_int32(0)
+    _check("spear_workspace_timeouts", load().spear_workspace_timeouts(_ptr(ws), ctypes.byref(out),
+                                                                       _stream(stream)))
+    return int(out.value)

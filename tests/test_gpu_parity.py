@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded bf16 inputs.  Packing, token selection and the one-hot unpack
+probe are bit-exact; fp32 outputs are within rel-L2 1e-3 and max-abs 2e-2."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_gemm_w4a16_amd import inputs as gen
+from quantized_gemm_w4a16_amd import spear as sp
+from gpu_util import (assert_close, dev, errors, gpu_ec, gpu_weights, host, run_gpu,
+                      run_oracle)
+
+pytestmark = pytest.mark.gpu
+
+ALL_PATHS_SMALL = [sp.PATH_DECODE, sp.PATH_DECODE_2PASS, sp.PATH_PREFILL]
+
+
+def test_library_is_in_tree():
+    lib = sp.load()
+    assert os.path.samefile(lib._name, sp.LIB_PATH)
+    assert torch.cuda.is_available()
+    print("[device]", torch.cuda.get_device_properties(0).gcnArchName, flush=True)
+
+
+# ------------------------------------------------------------------ packing
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_pack_bit_exact(cfg):
+    d = gen.make(cfg)
+    want, _ = oracle.pack_w4(d["codes"], d["kind"])
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = sp.spear_pack_w4(dev(d["codes"]), d["kind"], bad_codes=bad)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), want)
+    assert int(bad.item()) == 0
+
+
+@pytest.mark.parametrize("kind", [oracle.CODES_S4, oracle.CODES_U4])
+def test_pack_ragged_and_bad_codes(kind):
+    rng = np.random.default_rng(31 + kind)
+    N, K = 37, 96
+    if kind == oracle.CODES_S4:
+        codes = rng.integers(-128, 128, size=(N, K), dtype=np.int16).astype(np.int8)
+    else:
+        codes = rng.integers(0, 256, size=(N, K), dtype=np.int16).astype(np.uint8)
+    want, nbad = oracle.pack_w4(codes, kind)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = sp.spear_pack_w4(dev(codes), kind, bad_codes=bad)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got), want)
+    assert int(bad.item()) == nbad > 0
+
+
+# ---------------------------------------------------------------------- gate
+
+@pytest.mark.parametrize("M,K", [(0, 64), (1, 32), (5, 4096), (64, 4096), (1500, 1024)])
+@pytest.mark.parametrize("hard,tau", [(0, 0.5), (1, 0.5), (1, 0.35), (1, 1.0), (1, 0.0)])
+def test_gate_parity(M, K, hard, tau):
+    rng = np.random.default_rng(M * 7 + K + int(tau * 100) + hard)
+    x = gen.bf16_bits(rng.normal(0, 1, size=(M, K)).astype(np.float32))
+    wg = gen.bf16_bits(rng.normal(0, 1 / math.sqrt(K), size=K).astype(np.float32))
+    b = 0.125
+    ref = oracle.gate(x, wg, b, tau, hard)
+    if M and hard and 0 < tau < 1:
+        assert np.min(np.abs(ref["z"] - oracle.logit_threshold(tau))) > 1e-9
+    g, idx, n = sp.spear_gate(dev(x) if M else torch.empty((0, K), dtype=torch.int16,
+                                                          device="cuda"),
+                              dev(wg), b, tau, hard)
+    torch.cuda.synchronize()
+    n = int(n.item())
+    assert n == ref["n_active"]
+    assert np.array_equal(host(idx)[:n], ref["idx"])
+    if M:
+        np.testing.assert_allclose(host(g), ref["g"], rtol=2e-7, atol=0)
+
+
+# ----------------------------------------------------------- one-hot probe
+
+@pytest.mark.parametrize("path,M", [(sp.PATH_DECODE, 16), (sp.PATH_DECODE, 3),
+                                    (sp.PATH_DECODE_2PASS, 16), (sp.PATH_PREFILL, 16),
+                                    (sp.PATH_PREFILL, 40), (sp.PATH_PREFILL, 200)])
+@pytest.mark.parametrize("K", [256, 4096])
+def test_one_hot_unpack_probe(path, M, K):
+    """x[m] = e_{k_m}, s = 1: y[m][n] = u[n][k_m] - z_n exactly (fp32 output).  Pins
+    the in-kernel nibble order, the pair permutation and the offset removal."""
+    rng = np.random.default_rng(K + M + path)
+    N = 48
+    u = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+    z = rng.integers(0, 16, size=N, dtype=np.uint8)
+    ks = rng.choice(K, size=M, replace=M > K)
+    x = np.zeros((M, K), np.uint16)
+    x[np.arange(M), ks] = 0x3F80
+    d = {"M": M, "N": N, "K": K, "kind": oracle.CODES_U4, "codes": u,
+         "scales": np.ones(N, np.float32), "zeros": z, "x": x, "ec": None}
+    y, _ = run_gpu(d, path=path, ec=False)
+    want = u[:, ks].T.astype(np.float32) - z[None, :].astype(np.float32)
+    assert np.array_equal(y, want)
+
+
+# ----------------------------------------------------------- full workloads
+
+@pytest.mark.parametrize("path", ALL_PATHS_SMALL)
+@pytest.mark.parametrize("out", [sp.OUT_F32, sp.OUT_BF16])
+def test_c1(path, out):
+    d = gen.make(1)
+    ref = run_oracle(d)
+    y, e = run_gpu(d, path=path, out=out)
+    if out == sp.OUT_F32:
+        assert_close(y, ref, f"C1 path={path}")
+    else:
+        # bf16 output: within one bf16 ulp (of |ref|) of the oracle
+        a = np.maximum(np.abs(ref), 2.0 ** -120)
+        ulp = 2.0 ** (np.floor(np.log2(a)) - 7)
+        assert np.all(np.abs(y.astype(np.float64) - ref) <= ulp)
+        want = gen.bf16_bits(ref.astype(np.float32))
+        same = np.mean(gen.bf16_bits(y) == want)
+        print(f"[parity] C1 bf16 path={path} bit-equal to RNE(oracle): {same:.5f}")
+        assert same >= 0.999
+    gref = oracle.gate(d["x"], d["ec"]["w_g"], d["ec"]["b"], d["ec"]["tau"], d["ec"]["hard"])
+    np.testing.assert_allclose(host(e.g_out), gref["g"], rtol=2e-7)
+    assert int(e.n_active_out.item()) == 16
+
+
+@pytest.mark.parametrize("M", [1, 4, 8])
+@pytest.mark.parametrize("path", ALL_PATHS_SMALL)
+def test_c2_decode(M, path):
+    d = gen.make(2, M=M)
+    ref = run_oracle(d)
+    y, e = run_gpu(d, path=path)
+    assert_close(y, ref, f"C2 M={M} path={path}")
+    assert int(e.n_active_out.item()) == M
+    plain, _ = run_gpu(d, path=path, ec=False)
+    assert_close(plain, run_oracle(d, ec=None), f"C2 plain M={M} path={path}")
+
+
+def test_c3_hard_gate_selection():
+    d = gen.make(3)
+    ec = d["ec"]
+    gref = oracle.gate(d["x"], ec["w_g"], ec["b"], ec["tau"], ec["hard"])
+    t = oracle.logit_threshold(ec["tau"])
+    print(f"[C3] active {gref['n_active']}/64, margin {np.min(np.abs(gref['z'] - t)):.3e}")
+    ref = run_oracle(d)
+    y, e = run_gpu(d)
+    n = int(e.n_active_out.item())
+    assert n == gref["n_active"]
+    assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
+    np.testing.assert_allclose(host(e.g_out), gref["g"], rtol=2e-7)
+    assert_close(y, ref, "C3")
+
+
+def test_c4_full_size_sampled():
+    d = gen.make(4)
+    rng = np.random.default_rng(44)
+    S = 3000
+    ms = rng.integers(0, d["M"], S)
+    ns = rng.integers(0, d["N"], S)
+    ms[:64] = d["M"] - 1          # the last tile row and column
+    ns[64:128] = d["N"] - 1
+    packed, _ = oracle.pack_w4(d["codes"], d["kind"])
+    ref = oracle.w4_linear_sampled(d["x"], packed, d["scales"], d["zeros"], d["ec"], ms, ns)
+    y, e = run_gpu(d)
+    assert np.all(np.isfinite(y))
+    assert_close(y[ms, ns], ref, "C4 sampled")
+    assert int(e.n_active_out.item()) == d["M"]
+    plain, _ = run_gpu(d, ec=False)
+    ref0 = oracle.w4_linear_sampled(d["x"], packed, d["scales"], d["zeros"], None, ms, ns)
+    assert_close(plain[ms, ns], ref0, "C4 plain sampled")
+
+
+def random_case(M, N, K, r, kind, hard, seed):
+    rng = np.random.default_rng(seed)
+    if kind == oracle.CODES_S4:
+        codes, zeros = rng.integers(-8, 8, size=(N, K), dtype=np.int8), None
+    else:
+        codes = rng.integers(0, 16, size=(N, K), dtype=np.uint8)
+        zeros = rng.integers(0, 16, size=N, dtype=np.uint8)
+    x = gen.bf16_bits(rng.normal(0, 1, size=(M, K)).astype(np.float32))
+    ec = {"A": gen.bf16_bits(rng.normal(0, 0.05, size=(r, K)).astype(np.float32)),
+          "B": gen.bf16_bits(rng.normal(0, 0.05, size=(N, r)).astype(np.float32)),
+          "w_g": gen.bf16_bits(rng.normal(0, 1 / math.sqrt(K), size=K).astype(np.float32)),
+          "b": 0.1, "tau": 0.5, "hard": hard, "r": r}
+    return {"M": M, "N": N, "K": K, "kind": kind, "codes": codes,
+            "scales": rng.uniform(0.005, 0.02, N).astype(np.float32), "zeros": zeros,
+            "x": x, "ec": ec}
+
+
+RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 256),
+          (17, 1000, 160, 40), (33, 24, 4096, 8), (100, 200, 544, 64), (130, 129, 1024, 32),
+          (257, 300, 2080, 24)]
+
+
+@pytest.mark.parametrize("M,N,K,r", RAGGED)
+@pytest.mark.parametrize("kind", [oracle.CODES_S4, oracle.CODES_U4])
+@pytest.mark.parametrize("hard", [0, 1])
+def test_ragged_shapes(M, N, K, r, kind, hard):
+    d = random_case(M, N, K, r, kind, hard, seed=M * 1000 + N + K + r + kind * 7 + hard)
+    ref = run_oracle(d)
+    gref = oracle.gate(d["x"], d["ec"]["w_g"], d["ec"]["b"], d["ec"]["tau"], hard)
+    paths = ALL_PATHS_SMALL if M <= 16 else [sp.PATH_PREFILL]
+    for path in paths:
+        y, e = run_gpu(d, path=path)
+        assert_close(y, ref, f"ragged {M}x{N}x{K} r={r} kind={kind} hard={hard} path={path}")
+        n = int(e.n_active_out.item())
+        assert n == gref["n_active"]
+        assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
+
+
+@pytest.mark.parametrize("path,M", [(sp.PATH_DECODE, 1), (sp.PATH_DECODE, 16),
+                                    (sp.PATH_DECODE_2PASS, 8), (sp.PATH_PREFILL, 16),
+                                    (sp.PATH_PREFILL, 150)])
+def test_invariants_bitwise(path, M):
+    """tau = 1, A = 0 and b = -inf each reduce the layer to plain W4 bit for bit;
+    repeated calls are bitwise identical (no floating-point atomics)."""
+    d = random_case(M, 272, 1024, 32, oracle.CODES_U4, 0, seed=500 + M + path)
+    w = gpu_weights(d)
+    plain, _ = run_gpu(d, path=path, w=w, ec=False)
+    for mod in [dict(hard=1, tau=1.0), dict(A=np.zeros_like(d["ec"]["A"])),
+                dict(b=-math.inf)]:
+        y, _ = run_gpu(d, path=path, w=w, ec=dict(d["ec"], **mod))
+        assert np.array_equal(y, plain), mod
+    y1, _ = run_gpu(d, path=path, w=w)
+    y2, _ = run_gpu(d, path=path, w=w)
+    assert np.array_equal(y1, y2)
+    assert not np.array_equal(y1, plain)
+
+
+def test_rows_independent_of_batch():
+    d = random_case(12, 96, 512, 16, oracle.CODES_S4, 1, seed=77)
+    w = gpu_weights(d)
+    y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w)
+    for m in [0, 5, 11]:
+        dm = dict(d, M=1, x=d["x"][m:m + 1])
+        ym, _ = run_gpu(dm, path=sp.PATH_DECODE, w=w)
+        np.testing.assert_allclose(ym[0], y[m], rtol=0, atol=1e-5)
+
+
+def test_workspace_reuse_across_calls():
+    """One workspace serves a sequence of fused decode calls of different shapes
+    (the kernels return its counters to zero)."""
+    ws = sp.new_workspace(16, 1024, 4096, 64)
+    for (M, N, K, r) in [(1, 1024, 4096, 64), (16, 512, 2048, 32), (4, 1024, 4096, 64)]:
+        d = random_case(M, N, K, r, oracle.CODES_U4, 1, seed=M + N + K)
+        assert ws.numel() >= sp.spear_w4_linear_workspace_size(M, N, K, r)
+        y, _ = run_gpu(d, path=sp.PATH_DECODE, ws=ws)
+        assert_close(y, run_oracle(d), f"ws reuse {M}x{N}x{K}")
+    assert np.all(host(ws[:64]) == 0)
+
+
+def test_forced_wait_timeout_is_reported():
+    """A zero wait limit makes the fused epilogues give up at once: the call still
+    completes, each output is the plain or the compensated value, and the
+    expired waits are counted."""
+    d = random_case(4, 4096, 4096, 32, oracle.CODES_U4, 0, seed=9)
+    w = gpu_weights(d)
+    ws = sp.new_workspace(4, 4096, 4096, 32)
+    plain, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ec=False)
+    full, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
+    assert sp.spear_workspace_timeouts(ws) == 0
+    try:
+        sp.spear_set_wait_limit(1)
+        y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
+        n = sp.spear_workspace_timeouts(ws)
+    finally:
+        sp.spear_set_wait_limit(0)
+    ok = np.isclose(y, plain, rtol=0, atol=1e-6) | np.isclose(y, full, rtol=0, atol=1e-6)
+    assert np.all(ok)
+    print(f"[timeout] expired waits: {n}")
+    assert n >= 0
+    y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
+    assert np.array_equal(y, full)
+
+
+@pytest.mark.parametrize("M", [1, 16, 128, 2048])
+def test_c5_stack_layers_sampled(M):
+    ec_layer = gen.c5_ec_layers()[0]
+    for (layer, lin) in [(ec_layer, "down"), (ec_layer, "q"), (0 if ec_layer else 1, "up")]:
+        d = gen.make_c5(layer, lin, M)
+        rng = np.random.default_rng(M + layer)
+        S = 1500
+        ms, ns = rng.integers(0, M, S), rng.integers(0, d["N"], S)
+        packed, _ = oracle.pack_w4(d["codes"], d["kind"])
+        ref = oracle.w4_linear_sampled(d["x"], packed, d["scales"], d["zeros"], d["ec"], ms, ns)
+        y, e = run_gpu(d)
+        assert_close(y[ms, ns], ref, f"C5 {d['name']} M={M}")
+        if d["ec"] is not None:
+            gref = oracle.gate(d["x"], d["ec"]["w_g"], 0.0, 0.5, 1)
+            n = int(e.n_active_out.item())
+            assert n == gref["n_active"]
+            assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
