@@ -22,8 +22,16 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
     memset(&L, 0, sizeof L);
     const bool decode = M <= 16;
     L.ncg = cdiv(N, 16);
+    // Decode: a workgroup stages the activations of its K range in LDS
+    // (M rows of 128-deep super-steps, 256 bytes each plus 16 of padding) and
+    // its 4 waves take at most DEC_SW_MAX super-steps each.
     const int64_t S = cdiv(K, 128);
-    L.ksplit = cdiv(S, DEC_SPW);
+    const int64_t mr = M < 1 ? 1 : (M > 16 ? 16 : M);
+    int64_t smax = (DEC_LDS_MAX / (mr + 1) - 16) / 256;   // M + 1 rows (one of zeros)
+    if (smax > DEC_WAVES * DEC_SW_MAX)
+        smax = DEC_WAVES * DEC_SW_MAX;
+    L.ksplit = cdiv(S, smax);
+    L.spw = cdiv(S, L.ksplit);
     L.rpad = r > 0 ? cdiv(r, 32) * 32 : 0;
     L.mpad = cdiv(M > 0 ? M : 1, 16) * 16;
     int64_t nprod = cdiv(K, PROD_K);
@@ -272,6 +280,7 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
     a.K = K;
     a.ncg = L.ncg;
     a.ksplit = L.ksplit;
+    a.spw = L.spw;
     a.nprod = L.nprod;
     a.prod_k = L.prod_k;
     a.mpad = L.mpad;

@@ -14,20 +14,23 @@ namespace spear {
 namespace {
 
 // --------------------------------------------------------------------- pre-pass
-// One workgroup per 16 tokens; its 4 waves split K.  Per token: gate logit in
+// One workgroup per 16 tokens; its PRE_WAVES waves split K.  Per token: gate logit in
 // fp64, g, hard-gate flag, u = A x (fp32 via MFMA, natural depth order on both
 // operands), v = g u (0 for skipped tokens) stored as bf16 hi + lo.
-__global__ __launch_bounds__(256) void prepass_kernel(const LinearArgs a)
+constexpr int PRE_WAVES = 16;
+
+__global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArgs a)
 {
-    __shared__ f32x4 s_u[4][2][64];
-    __shared__ double s_z[4][64];
+    __shared__ f32x4 s_u[PRE_WAVES][2][64];
+    __shared__ double s_z[PRE_WAVES][64];
     __shared__ float s_g[16];
     __shared__ int s_act[16];
+    pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, K = a.K;
     const int64_t m0 = (int64_t)blockIdx.x * 16;
-    const int64_t T = K / 32, t0 = wave * T / 4, t1 = (wave + 1) * T / 4;
+    const int64_t T = K / 32, t0 = wave * T / PRE_WAVES, t1 = (wave + 1) * T / PRE_WAVES;
     const int64_t m = m0 + lr;
     const bool mv = m < M;
     const int rpad = a.rpad, r = a.r;
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(256) void prepass_kernel(const LinearArgs a)
         __syncthreads();
         if (jp == 0 && tid < 16) {
             double z = (double)a.b;
-            for (int w = 0; w < 4; w++)
+            for (int w = 0; w < PRE_WAVES; w++)
                 for (int q = 0; q < 4; q++)
                     z += s_z[w][tid + 16 * q];
             const int64_t mm = m0 + tid;
@@ -78,7 +81,7 @@ __global__ __launch_bounds__(256) void prepass_kernel(const LinearArgs a)
         __syncthreads();
         if (wave < 2) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            for (int w = 0; w < 4; w++)
+            for (int w = 0; w < PRE_WAVES; w++)
                 u += s_u[w][wave][lane];
             // lane holds u[rank 32 jp + 16 wave + 4 lg + i][token m0 + lr]
             const float g = s_act[lr] ? s_g[lr] : 0.f;
@@ -106,10 +109,10 @@ __global__ __launch_bounds__(256) void prepass_kernel(const LinearArgs a)
 // Output tile BN channels x BM tokens, computed as W x^T so each lane ends with
 // 4 consecutive channels of one token (contiguous stores).  K advances in
 // 128-deep super-steps.  Packed weights: HBM -> registers (16-byte loads, one
-// super-step of prefetch), unpacked to bf16 128+u pairs in registers.
+// super-step of prefetch), unpacked to bf16 (1 + u/16) pairs in registers.
 // Activations: HBM -> registers -> LDS (double-buffered), permuted on the way
 // to match the unpacked pair order, and summed per token for the epilogue's
-// offset removal.  Epilogue: y = s_n (acc - (128 + z_n) sum_k x) + B v.
+// offset removal.  Epilogue: y = s_n (16 acc - (16 + z_n) sum_k x) + B v.
 template <int FN, int FM, int WNW, int WMW, int EC, int OUT_F32>
 __global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a)
 {
@@ -121,6 +124,7 @@ __global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a
     __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * RS];
     __shared__ float s_rs[BM];
 
+    pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int wn = wave % WNW, wm = wave / WNW;
@@ -143,6 +147,20 @@ __global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a
 #pragma unroll
     for (int i = 0; i < CPT; i++)
         rsp[i] = 0.f;
+
+    // Epilogue operands, loaded now without branches and used at the end.
+    float sc_raw[FN][4];
+    uint32_t z_raw[FN][4];
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int64_t nn = n0 + (wn * FN + fn) * 16 + 4 * lg + i;
+            nn = nn < N ? nn : N - 1;
+            sc_raw[fn][i] = a.scales[nn];
+            z_raw[fn][i] = load_zero_byte(a.zeros, a.scales, nn);
+        }
+    }
 
     u32x4 wc[FN], wx[FN];
     f32x4 acc[FN][FM];
@@ -232,16 +250,12 @@ __global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a
     for (int fn = 0; fn < FN; fn++) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const int64_t nn = n0 + (wn * FN + fn) * 16 + 4 * lg + i;
-            float sn = 0.f, zc = 0.f;
-            if (nn < N) {
-                sn = a.scales[nn];
-                zc = 128.f + (a.zeros ? (float)a.zeros[nn] : 8.f);
-            }
+            const float sn = sc_raw[fn][i];
+            const float zc = UNPACK_OFF + zero_point(a.zeros, z_raw[fn][i]);
 #pragma unroll
             for (int fm = 0; fm < FM; fm++) {
                 const float rsm = s_rs[(wm * FM + fm) * 16 + lr];
-                acc[fn][fm][i] = sn * __builtin_fmaf(-zc, rsm, acc[fn][fm][i]);
+                acc[fn][fm][i] = sn * __builtin_fmaf(-zc, rsm, UNPACK_SCALE * acc[fn][fm][i]);
             }
         }
     }
@@ -338,7 +352,8 @@ hipError_t launch_gemm_t(const LinearArgs &a, int ec_on, hipStream_t s)
 
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)((a.M + 15) / 16)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)((a.M + 15) / 16)), dim3(64 * PRE_WAVES), 0,
+                       s, a);
     return hipGetLastError();
 }
 

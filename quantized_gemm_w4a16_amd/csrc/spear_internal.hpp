@@ -28,20 +28,29 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c)
 }
 
 // 8 packed nibbles (depth positions 0..7, position i in bits 4i..4i+3) ->
-// bf16 pairs holding 128 + u exactly (bf16 has unit spacing on [128, 256)).
-// Pair p carries positions (p, p + 4): (0,4) (1,5) (2,6) (3,7).  The zero
-// point and the 128 offset are removed in the epilogue: sum x (128 + u) -
-// (128 + z) sum x = sum x (u - z).
+// bf16 pairs holding 1 + u/16 exactly: the nibble becomes the top 4 of the 7
+// mantissa bits of a value in [1, 2).  Pair p carries positions (p, p + 4):
+// (0,4) (1,5) (2,6) (3,7).  The epilogue removes the offset and the zero point:
+// 16 sum x (1 + u/16) - (16 + z) sum x = sum x (u - z).  Keeping the nibble in
+// the high mantissa bits keeps that offset small (16 sum x).
 __device__ __forceinline__ u32x4 unpack8(uint32_t w)
 {
-    const uint32_t m = 0x000F000Fu, c = 0x43004300u;
+    // The mask and the exponent bits go through registers so that each output
+    // is one shift and one v_and_or_b32 (two literals cannot share one VOP3).
+    uint32_t m, c;
+    asm("s_mov_b32 %0, 0x780078" : "=s"(m));
+    asm("v_mov_b32 %0, 0x3f803f80" : "=v"(c));
     u32x4 r;
-    r[0] = (w & m) | c;
-    r[1] = ((w >> 4) & m) | c;
-    r[2] = ((w >> 8) & m) | c;
-    r[3] = ((w >> 12) & m) | c;
+    r[0] = ((w << 3) & m) | c;
+    r[1] = ((w >> 1) & m) | c;
+    r[2] = ((w >> 5) & m) | c;
+    r[3] = ((w >> 9) & m) | c;
     return r;
 }
+
+// Scale of the unpacked value and the offset it carries: unpacked = (OFF + u) / SCALE.
+constexpr float UNPACK_SCALE = 16.0f;
+constexpr float UNPACK_OFF = 16.0f;
 
 // 8 bf16 in natural order (pairs (0,1) (2,3) (4,5) (6,7)) -> the pair order
 // unpack8 produces: (0,4) (1,5) (2,6) (3,7).
@@ -77,15 +86,40 @@ __device__ __forceinline__ uint16_t f2bf(float f)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// sum of the 8 bf16 in d (fp32 accumulate).
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t v)
+{
+    // element-wise bit casts of vector lanes miscompile with this toolchain;
+    // copy through a scalar instead
+    bf16x2 r;
+    __builtin_memcpy(&r, &v, sizeof r);
+    return r;
+}
+
+// sum of the 8 bf16 in d (fp32 accumulate, two per dot2).
 __device__ __forceinline__ float sum8(u32x4 d, float acc)
 {
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d[0]), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d[1]), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d[2]), one, acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, d[3]), one, acc, false);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+        const uint32_t t = d[e];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(t), one, acc, false);
+    }
     return acc;
+}
+
+// Zero points are read without a branch (a load under a branch makes the
+// compiler wait for every outstanding load where the branch ends): with no
+// zero points the byte is read from the scales array, which is always valid
+// and at least N bytes long, and replaced by 8 where it is used.
+__device__ __forceinline__ uint32_t load_zero_byte(const uint8_t *zeros, const float *scales,
+                                                   int64_t n)
+{
+    const uint8_t *p = zeros ? zeros : reinterpret_cast<const uint8_t *>(scales);
+    return p[n];
+}
+__device__ __forceinline__ float zero_point(const uint8_t *zeros, uint32_t raw)
+{
+    return zeros ? (float)raw : 8.f;
 }
 
 // Agent-scope atomics on workspace counters.
@@ -117,15 +151,15 @@ enum {
     HDR_WORDS = 64
 };
 
-constexpr int DEC_WAVES = 4;    // decode workgroup: 4 waves split the K range
-constexpr int DEC_SW = 2;       // 128-deep super-steps per decode wave
-constexpr int DEC_SPW = DEC_WAVES * DEC_SW;  // super-steps per decode workgroup
+constexpr int DEC_WAVES = 4;        // decode workgroup: 4 waves split its K range
+constexpr int DEC_SW_MAX = 8;       // 128-deep super-steps per decode wave, at most
+constexpr int DEC_LDS_MAX = 81920;  // LDS bytes of staged activations (M + 1 rows), at most
 constexpr int PROD_K = 256;     // preferred K slice of one EC producer
 constexpr int MAX_PROD = 64;    // at most this many producers (slices grow beyond)
 
 struct WsLayout {
     size_t hdr, colcnt, splitp, produ, prodz, vhi, vlo, active, total;
-    int64_t ncg, ksplit, nprod, prod_k, rpad, mpad;
+    int64_t ncg, ksplit, spw, nprod, prod_k, rpad, mpad;
 };
 
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r);
@@ -147,11 +181,48 @@ struct LinearArgs {
     int32_t hard;
     int32_t r, rpad;
     int64_t M, N, K;
-    int64_t ncg, ksplit, nprod, prod_k, mpad;
+    int64_t ncg, ksplit, spw, nprod, prod_k, mpad;
     WsLayout L;
     uint32_t wait_limit;
     int32_t out_f32;
 };
+
+// Explicit counter waits (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
+// expcnt 6:4, lgkmcnt 11:8) and a barrier without the fence of
+// __syncthreads, for code that orders its memory operations itself.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+__device__ __forceinline__ void bare_barrier() { __builtin_amdgcn_s_barrier(); }
+
+// Load every kernel argument at entry.  The compiler otherwise fetches fields
+// of a large argument struct lazily, in several batches that each cost a
+// memory round trip before the first data load can be issued.
+template <typename T>
+__device__ __forceinline__ void pin_arg(const T &v)
+{
+    static_assert(sizeof(T) == 4 || sizeof(T) == 8, "scalar argument");
+    if constexpr (sizeof(T) == 8)
+        asm volatile("" ::"s"(__builtin_bit_cast(uint64_t, v)));
+    else
+        asm volatile("" ::"s"(__builtin_bit_cast(uint32_t, v)));
+}
+
+__device__ __forceinline__ void pin_args(const LinearArgs &a)
+{
+    pin_arg(a.x); pin_arg(a.packed); pin_arg(a.scales); pin_arg(a.zeros); pin_arg(a.A);
+    pin_arg(a.B); pin_arg(a.wg); pin_arg(a.y); pin_arg(a.ws); pin_arg(a.g_out);
+    pin_arg(a.idx_out); pin_arg(a.nact_out); pin_arg(a.thr); pin_arg(a.b); pin_arg(a.hard);
+    pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
+    pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
+    pin_arg(a.L.hdr); pin_arg(a.L.colcnt); pin_arg(a.L.splitp); pin_arg(a.L.produ);
+    pin_arg(a.L.prodz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
+    pin_arg(a.wait_limit); pin_arg(a.out_f32);
+}
 
 hipError_t launch_pack(const void *codes, int32_t kind, int64_t N, int64_t K, uint8_t *packed,
                        int32_t *bad, hipStream_t s);
