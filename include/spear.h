@@ -143,7 +143,12 @@ size_t spear_w4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r
 
 /*
  * spear_workspace_init -- zero a workspace before its first use (a workspace
- * allocated zero-filled needs no init).  The kernels leave it in that state.
+ * allocated zero-filled needs no init).  Between calls the workspace holds
+ * library state: a launch counter that every fused decode launch advances (its
+ * producers tag the partial results they hand to the epilogues with it) and
+ * the tagged partials themselves, so it is zeroed once, not per call, and
+ * must not be modified by the caller afterwards.  Tags repeat after 2^32
+ * fused launches on one workspace; re-initialise it before that.
  * ws: device pointer, 256-byte aligned; bytes >= 256.
  */
 spear_status spear_workspace_init(void *ws, size_t bytes, void *stream);
@@ -175,7 +180,7 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
                                   void *stream);
 
 /*
- * The fused decode kernel's epilogue waits (bounded) for the EC vector that
+ * The fused decode kernel's epilogue waits (bounded) for the EC partials that
  * other workgroups of the same launch produce.  If a wait exceeds the limit
  * the affected outputs are written without the EC and a counter in the
  * workspace is incremented.  spear_set_wait_limit sets the limit in polling

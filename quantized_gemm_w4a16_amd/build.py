@@ -12,8 +12,13 @@ LIB = os.path.join(HERE, "libspear.so")
 SOURCES = ["api.hip", "pack_gate.hip", "decode.hip", "prefill.hip"]
 ARCH = "gfx950"
 # Packed fp32 arithmetic is left to nothing: it is disabled for all device code.
+# The atomic optimizer turns a one-lane atomic with a uniform address into a
+# wave scan that waits for the result (and every older load) at once; the
+# decode kernels issue their epoch claim behind the weight stream and need it
+# only at the end, so it stays a plain atomic.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
-          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]
 
 
 def _hipcc():

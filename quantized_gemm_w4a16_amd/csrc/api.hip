@@ -16,11 +16,26 @@ namespace spear {
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// EC producers of the fused decode: each workgroup's 4 waves take one K slice
+// of *prod_k each, and there are enough workgroups that each reads about
+// PROD_BYTES of A times ceil(M / 2).  A workgroup with more tokens streams
+// longer (its activations take more LDS traffic), so its producers may read
+// more each; fewer producers keep the partials every epilogue loads
+// (producers x tokens x ranks) small.
+static int64_t ec_producers(int64_t mr, int64_t K, int64_t rpad, int64_t *prod_k)
+{
+    int64_t nprod = cdiv(K * rpad * 2, PROD_BYTES * cdiv(mr, 2));
+    nprod = nprod < 1 ? 1 : (nprod > MAX_PROD ? MAX_PROD : nprod);
+    const int64_t most = cdiv(K, DEC_WAVES * 32);           // slices at least 32 deep
+    nprod = nprod > most ? most : nprod;
+    *prod_k = cdiv(cdiv(K, DEC_WAVES * nprod), 32) * 32;
+    return cdiv(K, DEC_WAVES * *prod_k);
+}
+
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
 {
     WsLayout L;
     memset(&L, 0, sizeof L);
-    const bool decode = M <= 16;
     L.ncg = cdiv(N, 16);
     // Decode: a workgroup stages the activations of its K range in LDS
     // (M rows of 128-deep super-steps, 256 bytes each plus 16 of padding) and
@@ -34,29 +49,31 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
     L.spw = cdiv(S, L.ksplit);
     L.rpad = r > 0 ? cdiv(r, 32) * 32 : 0;
     L.mpad = cdiv(M > 0 ? M : 1, 16) * 16;
-    int64_t nprod = cdiv(K, PROD_K);
-    const int64_t nwg = L.ncg * L.ksplit;
-    if (nprod > nwg)
-        nprod = nwg;
-    if (nprod > MAX_PROD)
-        nprod = MAX_PROD;
-    L.prod_k = cdiv(cdiv(K, nprod), 32) * 32;
-    L.nprod = cdiv(K, L.prod_k);
+    L.nprod = r > 0 ? ec_producers(mr, K, L.rpad, &L.prod_k) : 0;
+    // The partials region is sized for the most producers any token count
+    // uses (one token), so that a workspace sized for some M also serves every
+    // smaller M, and the decode path after the prefill path.
+    int64_t pk1 = 0;
+    const int64_t nprod_max = r > 0 ? ec_producers(1, K, L.rpad, &pk1) : 0;
 
     size_t off = 0;
     L.hdr = off;
     off = align256(off + HDR_WORDS * sizeof(uint32_t));
+    L.epoch = off;
+    off = align256(off + (size_t)EPOCH_CTRS * EPOCH_STRIDE);
     L.colcnt = off;
     off = align256(off + (size_t)L.ncg * sizeof(uint32_t));
     L.splitp = off;
-    if (decode && L.ksplit > 1)
+    if (L.ksplit > 1)                                     // any M: a larger M never needs less
         off = align256(off + (size_t)(L.ncg * L.ksplit * 64 * 5) * sizeof(float));
-    L.produ = off;
-    L.prodz = off;
-    if (decode && r > 0) {
-        off = align256(off + (size_t)(L.nprod * 16 * L.rpad) * sizeof(float));
-        L.prodz = off;
-        off = align256(off + (size_t)(L.nprod * 16) * sizeof(double));
+    // Producer partials, tagged 64-bit words {value, launch epoch}: u per
+    // (producer, token slot, rank) and the fp64 gate logit as two words.
+    L.pu = off;
+    L.pz = off;
+    if (r > 0) {
+        off = align256(off + (size_t)(nprod_max * 16 * L.rpad) * sizeof(uint64_t));
+        L.pz = off;
+        off = align256(off + (size_t)(nprod_max * 16 * 2) * sizeof(uint64_t));
     }
     L.vhi = L.vlo = L.active = off;
     if (r > 0) {

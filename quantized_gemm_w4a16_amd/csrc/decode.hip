@@ -12,25 +12,33 @@
 //  * a workgroup owns 16 output channels and a K range (all of K unless the
 //    activations of the range would not fit in LDS).  Its 4 stream waves load
 //    the activations of the range straight into LDS (global_load_lds), then
-//    issue every 16-byte load of their packed-weight share (HBM -> registers),
-//    wait once, and contract on bf16 MFMA (activations permuted to the unpack
-//    order as they leave LDS) with the tokens (padded to 16) as the MFMA's N
-//    side.  A second MFMA against a
-//    constant-one operand gives the per-token activation sums that remove the
-//    unpack offset in the epilogue.
+//    issue every 16-byte load of their packed-weight share (HBM -> registers)
+//    and contract on bf16 MFMA as each load lands (activations permuted to the
+//    unpack order in LDS), with the tokens (padded to 16) as the MFMA's N
+//    side.  A second MFMA against a constant-one operand gives the per-token
+//    activation sums that remove the unpack offset in the epilogue.
 //  * When K is split over workgroups, the last one of a channel group (atomic
 //    counter) sums the partial tiles in slice order (deterministic).
-//  * EC (fused mode): every workgroup has a fifth wave.  The first `nprod`
-//    of these to start (atomic ticket: the election follows actual start
-//    order) each compute the gate logit (fp64) and A.x (MFMA) of all tokens
-//    over one K slice, publish them (release) and count themselves done.  The
-//    epilogue wave of each channel group polls that count (plain coherent
-//    loads, bounded), takes one acquire fence, reduces the slices in slice
-//    order, applies the gate and the hard-gate selection, forms v = g (A x) as
-//    bf16 hi + lo and adds B v with two MFMAs per 32 ranks.  Every epilogue
-//    computes the same v in the same order.  Producers never wait, so every
-//    wait ends.
-//  * The last wave to finish returns the counters to zero.
+//  * EC (fused mode): the lowest block indices, which the dispatcher places
+//    first, are `nprod` producer workgroups.  Each reads about 16 KB of A (so a
+//    producer's share of the memory system is no larger than a stream
+//    workgroup's and its result is ready before the stream ends), computes
+//    the gate-logit partial (fp64) and A.x (MFMA) of every token over its K
+//    slice, reduces its 4 waves in LDS and stores the partials as 64-bit words
+//    {value, launch epoch}, one relaxed device-coherent store each, then
+//    leaves.  The epilogue workgroup of each channel group loads the words of
+//    its tokens (relaxed device-coherent loads, the 4 waves splitting the
+//    producers), re-loads until every tag carries this launch's epoch
+//    (bounded), sums the producers in order, applies the gate and the
+//    hard-gate selection, forms v = g (A x) as bf16 hi + lo and adds B v with
+//    two MFMAs per 32 ranks.  Each word is validated on its own, so no fence
+//    or counter orders the exchange; every epilogue computes the same v in
+//    the same order, and producers never wait.
+//  * The launch epoch comes from a 64-bit counter in the workspace: block 0
+//    adds 2^32 - (grid - 1) and every other block adds 1, so a launch adds
+//    exactly 2^32 whatever its grid, and every block of the launch reads the
+//    same upper half.  Graph replays and calls of other shapes on the same
+//    workspace therefore never see a stale tag as current.
 #include "spear_internal.hpp"
 
 namespace spear {
@@ -38,17 +46,11 @@ namespace spear {
 namespace {
 
 constexpr int DEC_THREADS = 64 * DEC_WAVES;               // stream waves
-constexpr int PS = PROD_K / 32;                           // 32-deep steps of a producer chunk
 
 struct DecShared {
     float red[DEC_WAVES][64][5];
     uint32_t u32[4];
 };
-
-__device__ __forceinline__ uint32_t *hdr_of(const LinearArgs &a)
-{
-    return reinterpret_cast<uint32_t *>(a.ws + a.L.hdr);
-}
 
 __device__ __forceinline__ void release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
@@ -64,23 +66,86 @@ __device__ __forceinline__ double dot8_f64(u32x4 x, u32x4 w, double acc)
     return acc;
 }
 
-// Producer wave for K slice p: partial gate logits z[m] (fp64) and partial
-// u[m][j] = sum_k A[j][k] x[m][k] (fp32) over the slice, for all 16 token slots.
-__device__ void ec_produce_wave(const LinearArgs &a, uint32_t p, int lane)
+// ------------------------------------------------------------------ fused EC
+constexpr int PCH = 256;                                  // producer K chunk per pass
+constexpr int PS = PCH / 32;                              // 32-deep MFMA steps of a chunk
+constexpr size_t EC_LDS_U = DEC_WAVES * 64 * 8 * sizeof(float);   // u partials of 4 waves
+static_assert(EC_LDS_U >= DEC_WAVES * 16 * 32 * sizeof(float), "consumer u exchange");
+constexpr size_t EC_LDS_Z = DEC_WAVES * 64 * sizeof(double);      // gate-logit partials
+constexpr size_t EC_LDS = EC_LDS_U + EC_LDS_Z + 64;               // + tag and flags
+
+// One atomic add per workgroup.  Block b claims on counter b % EPOCH_CTRS and
+// a launch adds exactly 2^32 to every counter: the first block of each class
+// adds 2^32 - (n - 1), the n - 1 others of the class 1 each, and block 0 adds
+// 2^32 to the counters no block of a small grid uses.  Between launches all
+// counters hold the same multiple of 2^32, so every block of a launch reads the
+// same upper half whatever the order of the adds.
+__device__ __forceinline__ uint64_t epoch_claim(const LinearArgs &a)
 {
-    const int lr = lane & 15, lg = lane >> 4;
+    uint8_t *base = a.ws + a.L.epoch;
+    const uint32_t G = gridDim.x, bid = blockIdx.x, c = bid % EPOCH_CTRS;
+    uint64_t add = 1;
+    if (bid < EPOCH_CTRS)
+        add = (1ull << 32) - ((G - 1 - c) / EPOCH_CTRS + 1) + 1;
+    if (bid == 0)
+        for (uint32_t cc = G; cc < EPOCH_CTRS; cc++)
+            __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(base + (size_t)cc * EPOCH_STRIDE),
+                                   1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(base + (size_t)c * EPOCH_STRIDE), add,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Tag of the launch (a zeroed workspace holds tag 0, which no launch uses).
+__device__ __forceinline__ uint32_t epoch_tag(uint64_t claimed) { return (uint32_t)(claimed >> 32) + 1u; }
+
+// A zero the compiler cannot see through.  The epoch claim returns into two
+// registers long before its value is used; with a literal zero on the other
+// path the tag arithmetic is folded (or hoisted) to right behind the atomic,
+// and a dead low half lets its register be reused, and each of these makes the
+// wave wait for the atomic and every older load there.  Adding this opaque
+// zero at the use keeps the arithmetic, and both registers, where they belong.
+__device__ __forceinline__ uint64_t opaque_zero64()
+{
+    uint32_t lo, hi;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lo));
+    asm volatile("v_mov_b32 %0, 0" : "=v"(hi));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ void store_tagged(uint64_t *p, uint32_t bits, uint32_t tag)
+{
+    __hip_atomic_store(p, ((uint64_t)tag << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_tagged(const uint64_t *p)
+{
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Producer workgroup p: wave w takes K slice [(4p + w) prod_k, +prod_k) and
+// computes, for all 16 token slots, the gate-logit partial (fp64) and
+// u[m][j] = sum_k A[j][k] x[m][k] (MFMA, fp32).  The waves are summed in order
+// in LDS and wave 0 stores the rows of the M real tokens as tagged words.
+__device__ void ec_produce(const LinearArgs &a, int64_t p, int wave, int lane, uint8_t *lds)
+{
+    const int tid = threadIdx.x, lr = lane & 15, lg = lane >> 4;
     const int64_t K = a.K, M = a.M;
-    const int64_t k0 = (int64_t)p * a.prod_k;
-    const int64_t k1 = (k0 + a.prod_k < K) ? k0 + a.prod_k : K;
-    float *produ = reinterpret_cast<float *>(a.ws + a.L.produ);
-    double *prodz = reinterpret_cast<double *>(a.ws + a.L.prodz);
     const int rpad = a.rpad, r = a.r;
+    uint64_t claimed = opaque_zero64();
+    if (tid == 0)
+        claimed = epoch_claim(a);                         // back long before it is used
+
+    const int64_t k0 = (p * DEC_WAVES + wave) * a.prod_k;
+    const int64_t k1 = (k0 + a.prod_k < K) ? k0 + a.prod_k : K;
+    float *lu = reinterpret_cast<float *>(lds);
+    double *lz = reinterpret_cast<double *>(lds + EC_LDS_U);
+    uint32_t *ltag = reinterpret_cast<uint32_t *>(lds + EC_LDS_U + EC_LDS_Z);
+    uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.L.pu);
+    uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.L.pz);
 
     double zp = 0.0;
     for (int jp = 0; jp < rpad / 32; jp++) {
         f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
         const int j0 = 32 * jp + lr, j1 = j0 + 16;
-        for (int64_t kc = k0; kc < k1; kc += PROD_K) {
+        for (int64_t kc = k0; kc < k1; kc += PCH) {
             u32x4 xf[PS], a0[PS], a1[PS];
 #pragma unroll
             for (int t = 0; t < PS; t++) {
@@ -106,122 +171,210 @@ __device__ void ec_produce_wave(const LinearArgs &a, uint32_t p, int lane)
             }
         }
         // u0: ranks 32 jp + 4 lg + i, u1: ranks 32 jp + 16 + 4 lg + i; token lr
-        float *dst = produ + ((int64_t)p * 16 + lr) * rpad + 32 * jp + 4 * lg;
-        *reinterpret_cast<f32x4 *>(dst) = u0;
-        *reinterpret_cast<f32x4 *>(dst + 16) = u1;
-    }
-    // z for token lr: the four lane groups in order
-    const double z1 = __shfl(zp, lr + 16), z2 = __shfl(zp, lr + 32), z3 = __shfl(zp, lr + 48);
-    if (lg == 0)
-        prodz[(int64_t)p * 16 + lr] = ((zp + z1) + z2) + z3;
-    release_agent();
-    if (lane == 0)
-        __hip_atomic_fetch_add(&hdr_of(a)[HDR_PROD_DONE], 1u, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Epilogue EC term (fused mode), wave 0 of the finishing workgroup: returns
-// e[i] for channel n0 + 4 lg + i and token lr, and writes the gate outputs
-// when this is channel group 0.
-__device__ f32x4 ec_epilogue_fused(const LinearArgs &a, const u32x4 *bpre, int64_t cg, int lane,
-                                   bool *ok_out)
-{
-    const int lr = lane & 15, lg = lane >> 4;
-    const int64_t M = a.M, N = a.N;
-    const int64_t n = cg * 16 + lr;
-    uint32_t *hdr = hdr_of(a);
-    f32x4 e = {0.f, 0.f, 0.f, 0.f};
-
-    uint32_t f = 0;
-    if (lane == 0) {
-        uint32_t it = 0;
-        while ((f = __hip_atomic_load(&hdr[HDR_PROD_DONE], __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT)) < (uint32_t)a.nprod) {
-            if (++it > a.wait_limit) {
-                atomicAdd(&hdr[HDR_TIMEOUTS], 1u);
-                break;
-            }
-            __builtin_amdgcn_s_sleep(2);
+        float *mine = lu + (wave * 64 + lane) * 8;
+        *reinterpret_cast<f32x4 *>(mine) = u0;
+        *reinterpret_cast<f32x4 *>(mine + 4) = u1;
+        if (jp == 0) {
+            lz[wave * 64 + lane] = zp;
+            if (tid == 0)
+                *ltag = epoch_tag(claimed + opaque_zero64());   // not hoisted to the atomic
         }
-    }
-    f = __shfl(f, 0);
-    *ok_out = f >= (uint32_t)a.nprod;
-    if (!*ok_out)
-        return e;
-    acquire_agent();
-
-    const double *prodz = reinterpret_cast<const double *>(a.ws + a.L.prodz);
-    const float *produ = reinterpret_cast<const float *>(a.ws + a.L.produ);
-    const int64_t np = a.nprod;
-    const int rpad = a.rpad, r = a.r;
-
-    // Gate of token lr: slices summed in order.
-    double z = (double)a.b;
-    for (int64_t p0 = 0; p0 < np; p0 += 16) {
-        double zz[16];
+        __syncthreads();
+        if (wave == 0) {
+            f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-        for (int i = 0; i < 16; i++)
-            zz[i] = (p0 + i < np) ? prodz[(p0 + i) * 16 + lr] : 0.0;
-#pragma unroll
-        for (int i = 0; i < 16; i++)
-            if (p0 + i < np)
-                z += zz[i];
-    }
-    const float g = (float)(1.0 / (1.0 + exp(-z)));
-    const int act = (lr < M) && (a.hard ? (z > a.thr) : 1);
-
-    if (cg == 0) {
-        const int a0 = (lane < 16) ? act : 0;
-        const uint64_t mask = __ballot(a0);
-        if (lane < 16 && lane < M && a.g_out)
-            a.g_out[lane] = g;
-        if (a0 && a.idx_out)
-            a.idx_out[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
-        if (lane == 0 && a.nact_out)
-            *a.nact_out = __popcll(mask);
-    }
-    if (__ballot(act) == 0ull)
-        return e;
-
-    for (int t = 0; t < rpad / 32; t++) {
-        const int j = 32 * t + 8 * lg;
-        // u[lr][j .. j+7], slices in order
-        f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = {0.f, 0.f, 0.f, 0.f};
-        for (int64_t p0 = 0; p0 < np; p0 += 8) {
-            f32x4 va[8], vb[8];
-#pragma unroll
-            for (int i = 0; i < 8; i++) {
-                const float *src = produ + ((p0 + i) * 16 + lr) * rpad + j;
-                const bool pv = p0 + i < np;
-                va[i] = pv ? *reinterpret_cast<const f32x4 *>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
-                vb[i] = pv ? *reinterpret_cast<const f32x4 *>(src + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+            for (int w = 0; w < DEC_WAVES; w++) {
+                s0 += *reinterpret_cast<const f32x4 *>(lu + (w * 64 + lane) * 8);
+                s1 += *reinterpret_cast<const f32x4 *>(lu + (w * 64 + lane) * 8 + 4);
             }
+            const uint32_t tag = *ltag;
+            if (lr < M) {
+                uint64_t *dst = pu + (p * 16 + lr) * rpad + 32 * jp + 4 * lg;
 #pragma unroll
-            for (int i = 0; i < 8; i++) {
-                if (p0 + i < np) {
-                    ua += va[i];
-                    ub += vb[i];
+                for (int i = 0; i < 4; i++) {
+                    store_tagged(dst + i, __float_as_uint(s0[i]), tag);
+                    store_tagged(dst + 16 + i, __float_as_uint(s1[i]), tag);
+                }
+                if (jp == 0 && lg == 0) {
+                    // z of token lr: waves in order, the four lane groups of each in order
+                    double z = 0.0;
+                    for (int w = 0; w < DEC_WAVES; w++)
+                        z += ((lz[w * 64 + lr] + lz[w * 64 + lr + 16]) + lz[w * 64 + lr + 32]) +
+                             lz[w * 64 + lr + 48];
+                    const uint64_t zb = __builtin_bit_cast(uint64_t, z);
+                    store_tagged(pz + (p * 16 + lr) * 2, (uint32_t)zb, tag);
+                    store_tagged(pz + (p * 16 + lr) * 2 + 1, (uint32_t)(zb >> 32), tag);
                 }
             }
         }
-        u32x4 vh, vl;
-#pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const float v0 = act ? g * (q < 2 ? ua[2 * q] : ub[2 * q - 4]) : 0.f;
-            const float v1 = act ? g * (q < 2 ? ua[2 * q + 1] : ub[2 * q - 3]) : 0.f;
-            const uint16_t h0 = f2bf(v0), h1 = f2bf(v1);
-            vh[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-            vl[q] = (uint32_t)f2bf(v0 - bf16f(h0)) | ((uint32_t)f2bf(v1 - bf16f(h1)) << 16);
-        }
-        u32x4 bf;
-        if (t < 2)
-            bf = bpre[t == 0 ? 0 : 1];
-        else
-            bf = (n < N && j < r) ? ld16(a.B + n * r + j) : zero4();
-        e = mfma16(bf, vh, e);
-        e = mfma16(bf, vl, e);
+        __syncthreads();                                  // LDS reused by the next rank block
     }
-    return e;
+}
+
+// Epilogue EC term (fused mode), called by all 4 waves of the workgroup that
+// finishes channel group cg.  Wave w loads the words of producers
+// [w np / 4, (w + 1) np / 4) in batches of 8 words a lane: per 32-rank block,
+// lane l takes rank l % 32 of token rows l / 32 + 2 k, k < KM (consecutive
+// lanes, consecutive words) of 8 / KM producers, and the gate-logit words of
+// token l % 16 of producer l / 16 (+ 4); a batch is re-loaded until every tag is
+// this launch's.  The wave subtotals meet in LDS and wave 0 finishes.  KM is
+// ceil(M / 2) rounded up to a power of two.  Returns, in wave 0, e[i] for
+// channel 16 cg + 4 lg + i and token lr; *ok_out is false (and the term zero)
+// when a bounded wait expired.  Writes the gate outputs when cg == 0.
+template <int KM>
+__device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, int wave, int lane,
+                            uint8_t *lds, uint32_t tag, bool *ok_out)
+{
+    constexpr int SPB = 8 / KM;                             // producers per batch
+    const int lr = lane & 15, lg = lane >> 4;
+    const int64_t M = a.M, N = a.N, np = a.nprod;
+    const int64_t n = cg * 16 + lr;
+    const int rpad = a.rpad, r = a.r;
+    const uint64_t *pu = reinterpret_cast<const uint64_t *>(a.ws + a.L.pu);
+    const uint64_t *pz = reinterpret_cast<const uint64_t *>(a.ws + a.L.pz);
+    float *lu = reinterpret_cast<float *>(lds);               // [wave][token][32]
+    double *lz = reinterpret_cast<double *>(lds + EC_LDS_U);  // [wave][token]
+    int32_t *lok = reinterpret_cast<int32_t *>(lds + EC_LDS_U + EC_LDS_Z);
+    const int64_t p0 = np * wave / DEC_WAVES, p1 = np * (wave + 1) / DEC_WAVES;
+    const int col = lane & 31, rh = lane >> 5;
+    int64_t mrow[KM];
+#pragma unroll
+    for (int k = 0; k < KM; k++)
+        mrow[k] = rh + 2 * k < M ? rh + 2 * k : M - 1;      // rows >= M re-read row M - 1
+    const int64_t zm = lr < M ? lr : M - 1;
+
+    f32x4 e = {0.f, 0.f, 0.f, 0.f};
+    float g = 0.f;
+    int act = 0;
+    bool ok = true;
+    for (int t = 0; t < rpad / 32; t++) {
+        float us[KM];
+#pragma unroll
+        for (int k = 0; k < KM; k++)
+            us[k] = 0.f;
+        double zs = 0.0;                                    // token lr, producers lg (mod 4)
+        for (int64_t pc = p0; ok && pc < p1; pc += SPB) {
+            uint64_t wu[SPB][KM], wz[(SPB + 3) / 4][2];
+            for (uint32_t it = 0;; it++) {
+                bool good = true;
+#pragma unroll
+                for (int c = 0; c < SPB; c++) {
+                    const int64_t pp = (pc + c < p1) ? pc + c : p1 - 1;
+#pragma unroll
+                    for (int k = 0; k < KM; k++)
+                        wu[c][k] = load_tagged(pu + (pp * 16 + mrow[k]) * rpad + 32 * t + col);
+                }
+                if (t == 0) {
+#pragma unroll
+                    for (int j = 0; j < (SPB + 3) / 4; j++) {
+                        const int64_t q = pc + lg + 4 * j;
+                        const int64_t pp = q < p1 ? q : p1 - 1;
+                        wz[j][0] = load_tagged(pz + (pp * 16 + zm) * 2);
+                        wz[j][1] = load_tagged(pz + (pp * 16 + zm) * 2 + 1);
+                    }
+                }
+#pragma unroll
+                for (int c = 0; c < SPB; c++)
+#pragma unroll
+                    for (int k = 0; k < KM; k++)
+                        good &= (uint32_t)(wu[c][k] >> 32) == tag;
+                if (t == 0) {
+#pragma unroll
+                    for (int j = 0; j < (SPB + 3) / 4; j++)
+                        good &= (uint32_t)(wz[j][0] >> 32) == tag && (uint32_t)(wz[j][1] >> 32) == tag;
+                }
+                if (__all(good))
+                    break;
+                if (it >= a.wait_limit) {
+                    ok = false;
+                    if (lane == 0)
+                        atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+            if (!ok)
+                break;
+#pragma unroll
+            for (int c = 0; c < SPB; c++)
+                if (pc + c < p1)
+#pragma unroll
+                    for (int k = 0; k < KM; k++)
+                        us[k] += __uint_as_float((uint32_t)wu[c][k]);
+            if (t == 0) {
+#pragma unroll
+                for (int j = 0; j < (SPB + 3) / 4; j++)
+                    if (lg + 4 * j < SPB && pc + lg + 4 * j < p1)
+                        zs += __builtin_bit_cast(double, (uint64_t)(uint32_t)wz[j][0] |
+                                                              ((uint64_t)(uint32_t)wz[j][1] << 32));
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KM; k++)
+            if (rh + 2 * k < 16)
+                lu[(wave * 16 + rh + 2 * k) * 32 + col] = us[k];
+        if (t == 0) {
+            // the four lane groups of token lr, in order
+            const double z1 = __shfl(zs, lr + 16), z2 = __shfl(zs, lr + 32), z3 = __shfl(zs, lr + 48);
+            if (lg == 0)
+                lz[wave * 16 + lr] = ((zs + z1) + z2) + z3;
+        }
+        if (lane == 0)
+            lok[wave] = ok;
+        __syncthreads();
+        const bool all_ok = lok[0] && lok[1] && lok[2] && lok[3];
+        if (all_ok && wave == 0) {
+            if (t == 0) {
+                // Gate of token lr: producers summed in order.
+                double z = (double)a.b;
+                for (int w = 0; w < DEC_WAVES; w++)
+                    z += lz[w * 16 + lr];
+                g = (float)(1.0 / (1.0 + exp(-z)));
+                act = (lr < M) && (a.hard ? (z > a.thr) : 1);
+                if (cg == 0) {
+                    const int a0 = (lane < 16) ? act : 0;
+                    const uint64_t mask = __ballot(a0);
+                    if (lane < 16 && lane < M && a.g_out)
+                        a.g_out[lane] = g;
+                    if (a0 && a.idx_out)
+                        a.idx_out[__popcll(mask & ((1ull << lane) - 1ull))] = lane;
+                    if (lane == 0 && a.nact_out)
+                        *a.nact_out = __popcll(mask);
+                }
+            }
+            // u[lr][32 t + 8 lg + q]; rows >= M hold stale LDS and are not active
+            f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua;
+#pragma unroll
+            for (int w = 0; w < DEC_WAVES; w++) {
+                ua += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg);
+                ub += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg + 4);
+            }
+            const int j = 32 * t + 8 * lg;
+            u32x4 vh, vl;
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                const float v0 = act ? g * (q < 2 ? ua[2 * q] : ub[2 * q - 4]) : 0.f;
+                const float v1 = act ? g * (q < 2 ? ua[2 * q + 1] : ub[2 * q - 3]) : 0.f;
+                const uint16_t h0 = f2bf(v0), h1 = f2bf(v1);
+                vh[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                vl[q] = (uint32_t)f2bf(v0 - bf16f(h0)) | ((uint32_t)f2bf(v1 - bf16f(h1)) << 16);
+            }
+            u32x4 bf;
+            if (t < 2)
+                bf = bpre[t == 0 ? 0 : 1];
+            else
+                bf = (n < N && j < r) ? ld16(a.B + n * r + j) : zero4();
+            e = mfma16(bf, vh, e);
+            e = mfma16(bf, vl, e);
+        }
+        __syncthreads();                                  // LDS reused by the next rank block
+        if (!all_ok) {
+            ok = false;
+            break;
+        }
+    }
+    *ok_out = ok;
+    return ok ? e : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 template <int EC_MODE, int OUT_F32, int SW>
@@ -232,29 +385,16 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    uint32_t *hdr = hdr_of(a);
 
     // EC producers (fused mode) are the lowest block indices, which start first:
-    // each of their waves computes the partials of one K slice, then they leave.
+    // they store the partials of their K slices, then leave.
     int64_t bid = blockIdx.x;
     if (EC_MODE == 1) {
-        const int64_t npwg = (a.nprod + DEC_WAVES - 1) / DEC_WAVES;
-        if (bid < npwg) {
-            const int64_t p = bid * DEC_WAVES + wave;
-            if (p < a.nprod)
-                ec_produce_wave(a, (uint32_t)p, lane);
-            __syncthreads();
-            if (tid == 0) {
-                const uint32_t old = __hip_atomic_fetch_add(&hdr[HDR_DONE], 1u, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
-                if (old == gridDim.x - 1) {
-                    atomic_store_relaxed(&hdr[HDR_PROD_DONE], 0u);
-                    atomic_store_relaxed(&hdr[HDR_DONE], 0u);
-                }
-            }
+        if (bid < a.nprod) {
+            ec_produce(a, bid, wave, lane, s_x);
             return;
         }
-        bid -= npwg;
+        bid -= a.nprod;
     }
     const bool stream = true;
     const int64_t ksplit = a.ksplit, spw = a.spw;
@@ -325,10 +465,17 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         k = k < K ? k : K - 32;
         wr[i] = ld16(a.packed + nc * (K / 2) + k / 2);
     }
+    // Launch epoch (fused EC), claimed behind the weight loads so that its
+    // round trip overlaps the stream; it is first needed in the epilogue.
+    uint64_t claimed = opaque_zero64();
+    if (EC_MODE == 1 && tid == 0)
+        claimed = epoch_claim(a);
 
     // Wait for everything but the weight stream (the SW youngest loads) and for
     // the LDS zero fills, then make the activations visible to the workgroup.
-    // The weight loads stay in flight; each super-step waits for its own.
+    // The weight loads stay in flight; each super-step waits for its own.  (In
+    // the wave that claimed the epoch the claim is the youngest operation, so
+    // there the first weight load is waited for too; it is needed next.)
     wait_vmcnt<SW>();
     wait_lgkmcnt0();
     bare_barrier();
@@ -372,6 +519,8 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
             sh.red[wave][lane][i] = acc[i];
         sh.red[wave][lane][4] = rs0[0] + rs1[0];
     }
+    if (EC_MODE == 1 && tid == 0)
+        sh.u32[0] = epoch_tag(claimed + opaque_zero64());    // both halves live until here
     __syncthreads();
 
     // 7. Reduce the stream waves (fixed order).
@@ -424,7 +573,21 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         }
     }
 
-    // 9. Epilogue (wave 0): scale, offset removal, EC, store.
+    // 9. Epilogue: the EC term (fused mode: all 4 waves), then wave 0 scales,
+    //    removes the offset, adds the EC term and stores.
+    f32x4 ec_e = {0.f, 0.f, 0.f, 0.f};
+    if (EC_MODE == 1 && epi) {
+        bool ok;
+        const uint32_t tag = sh.u32[0];
+        if (M <= 2)
+            ec_e = ec_consume<1>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+        else if (M <= 4)
+            ec_e = ec_consume<2>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+        else if (M <= 8)
+            ec_e = ec_consume<4>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+        else
+            ec_e = ec_consume<8>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+    }
     if (epi && wave == 0) {
         float yv[4];
 #pragma unroll
@@ -434,11 +597,9 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
             yv[i] = nn < N ? sc_raw[i] * __builtin_fmaf(-zc, rst, UNPACK_SCALE * tot[i]) : 0.f;
         }
         if (EC_MODE == 1) {
-            bool ok;
-            const f32x4 e = ec_epilogue_fused(a, bpre, cg, lane, &ok);
 #pragma unroll
             for (int i = 0; i < 4; i++)
-                yv[i] += e[i];
+                yv[i] += ec_e[i];
         } else if (EC_MODE == 2) {
             // v precomputed by the pre-pass (bf16 hi + lo, zero for skipped tokens)
             const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
@@ -491,18 +652,6 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
             }
         }
     }
-
-    // 10. Completion count (fused mode): the last workgroup restores the counters.
-    //     Every counter access of this workgroup precedes this point (producers
-    //     count themselves done before they leave; the epilogue polls above).
-    if (EC_MODE == 1 && tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&hdr[HDR_DONE], 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        if (old == gridDim.x - 1) {
-            atomic_store_relaxed(&hdr[HDR_PROD_DONE], 0u);
-            atomic_store_relaxed(&hdr[HDR_DONE], 0u);
-        }
-    }
 }
 
 // Dynamic LDS beyond 64 KiB must be enabled per kernel once.
@@ -514,10 +663,12 @@ hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
         hipFuncAttributeMaxDynamicSharedMemorySize, DEC_LDS_MAX);
     if (e != hipSuccess)
         return e;
-    const int64_t npwg = EC_MODE == 1 ? (a.nprod + DEC_WAVES - 1) / DEC_WAVES : 0;
+    const int64_t npwg = EC_MODE == 1 ? a.nprod : 0;
     const dim3 grid((unsigned)(npwg + a.ncg * a.ksplit));
     const dim3 block(64 * DEC_WAVES);
-    const size_t lds = (size_t)(a.M + 1) * (size_t)(a.spw * 256 + 16);
+    size_t lds = (size_t)(a.M + 1) * (size_t)(a.spw * 256 + 16);
+    if (EC_MODE == 1 && lds < EC_LDS)
+        lds = EC_LDS;                                     // EC partials meet in the same LDS
     hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW>), grid, block, lds, s, a);
     return hipGetLastError();
 }

@@ -143,10 +143,6 @@ __device__ __forceinline__ void atomic_store_relaxed(uint32_t *p, uint32_t v)
 // ------------------------------------------------------------ workspace layout
 // Header: 64 uint32 counters, all zero between calls.
 enum {
-    HDR_TICKET = 0,    // decode: workgroup start order (producer election)
-    HDR_PROD_DONE = 1, // decode: producers finished
-    HDR_DONE = 2,      // decode: workgroups finished (the last one resets)
-    HDR_FLAG = 3,      // decode: EC vector published
     HDR_TIMEOUTS = 4,  // bounded waits that expired (cleared by the host query)
     HDR_WORDS = 64
 };
@@ -154,11 +150,17 @@ enum {
 constexpr int DEC_WAVES = 4;        // decode workgroup: 4 waves split its K range
 constexpr int DEC_SW_MAX = 8;       // 128-deep super-steps per decode wave, at most
 constexpr int DEC_LDS_MAX = 81920;  // LDS bytes of staged activations (M + 1 rows), at most
-constexpr int PROD_K = 256;     // preferred K slice of one EC producer
-constexpr int MAX_PROD = 64;    // at most this many producers (slices grow beyond)
+// Launch epoch of the fused decode: 64-bit counters, one per 128-byte line so
+// that the per-workgroup claims do not queue behind each other on one address.
+constexpr int EPOCH_CTRS = 64;
+constexpr int EPOCH_STRIDE = 128;
+
+constexpr int PROD_BYTES = 16384; // bytes of A an EC producer workgroup reads, about
+constexpr int MAX_PROD = 32;      // at most this many EC producer workgroups
+constexpr int PROD_CHUNK = 4;     // producer partials a consumer wave loads per batch
 
 struct WsLayout {
-    size_t hdr, colcnt, splitp, produ, prodz, vhi, vlo, active, total;
+    size_t hdr, epoch, colcnt, splitp, pu, pz, vhi, vlo, active, total;
     int64_t ncg, ksplit, spw, nprod, prod_k, rpad, mpad;
 };
 
@@ -219,8 +221,8 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.idx_out); pin_arg(a.nact_out); pin_arg(a.thr); pin_arg(a.b); pin_arg(a.hard);
     pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
     pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
-    pin_arg(a.L.hdr); pin_arg(a.L.colcnt); pin_arg(a.L.splitp); pin_arg(a.L.produ);
-    pin_arg(a.L.prodz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
+    pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.colcnt); pin_arg(a.L.splitp); pin_arg(a.L.pu);
+    pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);
 }
 

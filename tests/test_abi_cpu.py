@@ -51,6 +51,16 @@ def test_workspace_size_layout(lib):
     assert f(-1, 16, 32, 0) == 0 and f(1, 0, 32, 0) == 0 and f(1, 16, 16, 0) == 0
 
 
+def test_workspace_size_monotone_in_tokens(lib):
+    """A workspace sized for M tokens serves every smaller M (decode and prefill
+    share one allocation): the size never decreases as M grows."""
+    f = sp.spear_w4_linear_workspace_size
+    for (N, K, r) in [(4096, 4096, 32), (1024, 11008, 64), (512, 2048, 256), (17, 96, 8),
+                      (4096, 32768, 32), (64, 4096, 0)]:
+        sizes = [f(M, N, K, r) for M in list(range(1, 40)) + [64, 128, 2048, 4096]]
+        assert all(b >= a for a, b in zip(sizes, sizes[1:])), (N, K, r, sizes)
+
+
 A16 = 0x10000          # fake, suitably aligned device addresses: never dereferenced
 
 
