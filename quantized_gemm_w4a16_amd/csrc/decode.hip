@@ -49,6 +49,7 @@ constexpr int DEC_THREADS = 64 * DEC_WAVES;               // stream waves
 
 struct DecShared {
     float red[DEC_WAVES][64][5];
+    float xs[DEC_WAVES];        // one token: the activation sum of each wave's chunks
     uint32_t u32[4];
 };
 
@@ -211,6 +212,84 @@ __device__ void ec_produce(const LinearArgs &a, int64_t p, int wave, int lane, u
     }
 }
 
+// Producer workgroup p for one token (the GEMV decode): wave w takes K slice
+// [(4p + w) prod_k, +prod_k); lane l takes rank 32 jp + l % 32 and the 32-deep
+// half l / 32 of each 64-deep step, and contracts A's row with x by bf16 dot2
+// (fp32) -- a plain matrix-vector product, no MFMA.  Lane 0 and 32 carry the
+// gate-logit partial (fp64).  Halves, then waves, are summed in order.
+__device__ void ec_produce_gv(const LinearArgs &a, int64_t p, int wave, int lane, uint8_t *lds)
+{
+    const int tid = threadIdx.x, j = lane & 31, h = lane >> 5;
+    const int64_t K = a.K;
+    const int rpad = a.rpad, r = a.r;
+    uint64_t claimed = opaque_zero64();
+    if (tid == 0)
+        claimed = epoch_claim(a);                         // back long before it is used
+
+    const int64_t k0 = (p * DEC_WAVES + wave) * a.prod_k;
+    const int64_t k1 = (k0 + a.prod_k < K) ? k0 + a.prod_k : K;   // k1 - k0: multiple of 32
+    float *lu = reinterpret_cast<float *>(lds);                   // [wave][32]
+    double *lz = reinterpret_cast<double *>(lds + EC_LDS_U);      // [wave]
+    uint32_t *ltag = reinterpret_cast<uint32_t *>(lds + EC_LDS_U + EC_LDS_Z);
+    uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.L.pu);
+    uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.L.pz);
+
+    double zp = 0.0;
+    for (int jp = 0; jp < rpad / 32; jp++) {
+        const int rank = 32 * jp + j;
+        float u = 0.f;
+        for (int64_t kc = k0; kc < k1; kc += 64) {
+            const int64_t kk = kc + 32 * h;
+            const bool kv = kk < k1;
+            u32x4 xa[4], aa[4];
+#pragma unroll
+            for (int q = 0; q < 4; q++) {
+                xa[q] = kv ? ld16(a.x + kk + 8 * q) : zero4();
+                aa[q] = (kv && rank < r) ? ld16(a.A + (int64_t)rank * K + kk + 8 * q) : zero4();
+            }
+            if (jp == 0 && j == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; q++)
+                    zp = dot8_f64(xa[q], kv ? ld16(a.wg + kk + 8 * q) : zero4(), zp);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; q++)
+#pragma unroll
+                for (int e = 0; e < 4; e++)
+                    u = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(aa[q][e]), as_bf16x2(xa[q][e]), u,
+                                                        false);
+        }
+        const float u_other = __shfl(u, (lane + 32) & 63);
+        if (h == 0)
+            lu[wave * 32 + j] = u + u_other;              // half 0, then half 1
+        if (jp == 0) {
+            const double z_other = __shfl(zp, 32);
+            if (lane == 0)
+                lz[wave] = zp + z_other;
+            if (tid == 0)
+                *ltag = epoch_tag(claimed + opaque_zero64());   // not hoisted to the atomic
+        }
+        __syncthreads();
+        if (wave == 0 && h == 0) {
+            float sum = 0.f;
+#pragma unroll
+            for (int w = 0; w < DEC_WAVES; w++)
+                sum += lu[w * 32 + j];
+            const uint32_t tag = *ltag;
+            store_tagged(pu + p * 16 * rpad + 32 * jp + j, __float_as_uint(sum), tag);
+            if (jp == 0 && j == 0) {
+                double z = 0.0;
+                for (int w = 0; w < DEC_WAVES; w++)
+                    z += lz[w];
+                const uint64_t zb = __builtin_bit_cast(uint64_t, z);
+                store_tagged(pz + p * 16 * 2, (uint32_t)zb, tag);
+                store_tagged(pz + p * 16 * 2 + 1, (uint32_t)(zb >> 32), tag);
+            }
+        }
+        __syncthreads();                                  // LDS reused by the next rank block
+    }
+}
+
 // Epilogue EC term (fused mode), called by all 4 waves of the workgroup that
 // finishes channel group cg.  Wave w loads the words of producers
 // [w np / 4, (w + 1) np / 4) in batches of 8 words a lane: per 32-rank block,
@@ -218,10 +297,13 @@ __device__ void ec_produce(const LinearArgs &a, int64_t p, int wave, int lane, u
 // lanes, consecutive words) of 8 / KM producers, and the gate-logit words of
 // token l % 16 of producer l / 16 (+ 4); a batch is re-loaded until every tag is
 // this launch's.  The wave subtotals meet in LDS and wave 0 finishes.  KM is
-// ceil(M / 2) rounded up to a power of two.  Returns, in wave 0, e[i] for
+// ceil(M / 2) rounded up to a power of two.  With GV (one token) B v is taken
+// on the vector ALU in fp32: lane (c, g) forms the partial of channel c over
+// ranks 8 g .. 8 g + 7, the four partials meet by shuffles in order, and each
+// lane then picks its four output channels.  Returns, in wave 0, e[i] for
 // channel 16 cg + 4 lg + i and token lr; *ok_out is false (and the term zero)
 // when a bounded wait expired.  Writes the gate outputs when cg == 0.
-template <int KM>
+template <int KM, int GV>
 __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, int wave, int lane,
                             uint8_t *lds, uint32_t tag, bool *ok_out)
 {
@@ -342,30 +424,63 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                         *a.nact_out = __popcll(mask);
                 }
             }
-            // u[lr][32 t + 8 lg + q]; rows >= M hold stale LDS and are not active
-            f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua;
+            if constexpr (GV) {
+                // token 0's u[32 t + 8 lg + q], q = 0..7; lanes of other tokens drop out
+                const float g0 = __shfl(g, 0);
+                const int act0 = __shfl(act, 0);
+                f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua;
 #pragma unroll
-            for (int w = 0; w < DEC_WAVES; w++) {
-                ua += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg);
-                ub += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg + 4);
-            }
-            const int j = 32 * t + 8 * lg;
-            u32x4 vh, vl;
+                for (int w = 0; w < DEC_WAVES; w++) {
+                    ua += *reinterpret_cast<const f32x4 *>(lu + w * 16 * 32 + 8 * lg);
+                    ub += *reinterpret_cast<const f32x4 *>(lu + w * 16 * 32 + 8 * lg + 4);
+                }
+                const int j = 32 * t + 8 * lg;
+                u32x4 bf;
+                if (t < 2)
+                    bf = bpre[t == 0 ? 0 : 1];
+                else
+                    bf = (n < N && j < r) ? ld16(a.B + n * r + j) : zero4();
+                float ep = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const float v0 = act ? g * (q < 2 ? ua[2 * q] : ub[2 * q - 4]) : 0.f;
-                const float v1 = act ? g * (q < 2 ? ua[2 * q + 1] : ub[2 * q - 3]) : 0.f;
-                const uint16_t h0 = f2bf(v0), h1 = f2bf(v1);
-                vh[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
-                vl[q] = (uint32_t)f2bf(v0 - bf16f(h0)) | ((uint32_t)f2bf(v1 - bf16f(h1)) << 16);
+                for (int q = 0; q < 8; q++) {
+                    const float v = act0 ? g0 * (q < 4 ? ua[q] : ub[q - 4]) : 0.f;
+                    const uint32_t bw = bf[q / 2];
+                    const float bq = __uint_as_float((q & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
+                    ep = __builtin_fmaf(bq, v, ep);
+                }
+                // channel lr: the four rank groups in order
+                const float e1 = __shfl(ep, lr + 16), e2 = __shfl(ep, lr + 32),
+                            e3 = __shfl(ep, lr + 48), e0 = __shfl(ep, lr);
+                const float erow = ((e0 + e1) + e2) + e3;
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+                    e[i] += __shfl(erow, 4 * lg + i);
+            } else {
+                // u[lr][32 t + 8 lg + q]; rows >= M hold stale LDS and are not active
+                f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua;
+#pragma unroll
+                for (int w = 0; w < DEC_WAVES; w++) {
+                    ua += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg);
+                    ub += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg + 4);
+                }
+                const int j = 32 * t + 8 * lg;
+                u32x4 vh, vl;
+#pragma unroll
+                for (int q = 0; q < 4; q++) {
+                    const float v0 = act ? g * (q < 2 ? ua[2 * q] : ub[2 * q - 4]) : 0.f;
+                    const float v1 = act ? g * (q < 2 ? ua[2 * q + 1] : ub[2 * q - 3]) : 0.f;
+                    const uint16_t h0 = f2bf(v0), h1 = f2bf(v1);
+                    vh[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+                    vl[q] = (uint32_t)f2bf(v0 - bf16f(h0)) | ((uint32_t)f2bf(v1 - bf16f(h1)) << 16);
+                }
+                u32x4 bf;
+                if (t < 2)
+                    bf = bpre[t == 0 ? 0 : 1];
+                else
+                    bf = (n < N && j < r) ? ld16(a.B + n * r + j) : zero4();
+                e = mfma16(bf, vh, e);
+                e = mfma16(bf, vl, e);
             }
-            u32x4 bf;
-            if (t < 2)
-                bf = bpre[t == 0 ? 0 : 1];
-            else
-                bf = (n < N && j < r) ? ld16(a.B + n * r + j) : zero4();
-            e = mfma16(bf, vh, e);
-            e = mfma16(bf, vl, e);
         }
         __syncthreads();                                  // LDS reused by the next rank block
         if (!all_ok) {
@@ -377,7 +492,7 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
     return ok ? e : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
-template <int EC_MODE, int OUT_F32, int SW>
+template <int EC_MODE, int OUT_F32, int SW, int GV>
 __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs a)
 {
     __shared__ DecShared sh;
@@ -391,7 +506,10 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     int64_t bid = blockIdx.x;
     if (EC_MODE == 1) {
         if (bid < a.nprod) {
-            ec_produce(a, bid, wave, lane, s_x);
+            if constexpr (GV)
+                ec_produce_gv(a, bid, wave, lane, s_x);
+            else
+                ec_produce(a, bid, wave, lane, s_x);
             return;
         }
         bid -= a.nprod;
@@ -480,18 +598,60 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     wait_lgkmcnt0();
     bare_barrier();
 
-    // 5. Permute the activations in place to the unpack pair order, once.
-    for (int64_t m = 0; m < M; m++) {
+    // 5. Permute the activations in place to the unpack pair order, once.  One
+    //    token: also sum the activations of the range (each wave its chunks,
+    //    reduced across the wave in a fixed butterfly order).
+    if (GV) {
+        float xsum = 0.f;
         for (int64_t q = tid; q < cpr; q += DEC_THREADS) {
-            u32x4 *p = reinterpret_cast<u32x4 *>(s_x + m * rs_bytes + 16 * q);
-            *p = perm8(*p);
+            u32x4 *p = reinterpret_cast<u32x4 *>(s_x + 16 * q);
+            const u32x4 v = *p;
+            xsum = sum8(v, xsum);
+            *p = perm8(v);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1)
+            xsum += __shfl_xor(xsum, o);
+        if (lane == 0)
+            sh.xs[wave] = xsum;
+    } else {
+        for (int64_t m = 0; m < M; m++) {
+            for (int64_t q = tid; q < cpr; q += DEC_THREADS) {
+                u32x4 *p = reinterpret_cast<u32x4 *>(s_x + m * rs_bytes + 16 * q);
+                *p = perm8(*p);
+            }
         }
     }
     wait_lgkmcnt0();
     bare_barrier();
 
     // 6. Contraction (stream waves), each super-step as soon as its weights land.
-    if (stream) {
+    if (GV) {
+        // One token: a wavefront-reduction GEMV.  Lane (c, g) holds channel
+        // n0 + c and 32 consecutive k of each super-step; the unpacked pairs
+        // meet the permuted activation pairs in bf16 dot2 (fp32), one
+        // accumulator per 8-deep quarter.
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < SW; i++) {
+            const int sl = sl0 + i;
+            if (sl < s_count) {
+                u32x4 xr[4];
+#pragma unroll
+                for (int d = 0; d < 4; d++)
+                    xr[d] = *reinterpret_cast<const u32x4 *>(s_x + (16 * sl + 4 * lg + d) * 16);
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    const u32x4 uw = unpack8(wr[i][d]);
+#pragma unroll
+                    for (int q = 0; q < 4; q++)
+                        acc[d] = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(uw[q]),
+                                                                 as_bf16x2(xr[d][q]), acc[d], false);
+                }
+            }
+        }
+        sh.red[wave][lane][0] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    } else {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, rs0 = acc0, rs1 = acc0;
         const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
         const uint8_t *xrow = s_x + (lr < M ? lr : M) * rs_bytes;
@@ -523,10 +683,21 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         sh.u32[0] = epoch_tag(claimed + opaque_zero64());    // both halves live until here
     __syncthreads();
 
-    // 7. Reduce the stream waves (fixed order).
+    // 7. Reduce the stream waves (fixed order).  Afterwards lane (t, g) of
+    //    wave 0 holds channels n0 + 4 g + i of token t, and token t's sum of x.
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};
     float rst = 0.f;
-    if (wave == 0) {
+    if (GV && wave == 0) {
+        for (int w = 0; w < DEC_WAVES; w++) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int c = 4 * lg + i;
+                tot[i] += ((sh.red[w][c][0] + sh.red[w][c + 16][0]) + sh.red[w][c + 32][0]) +
+                          sh.red[w][c + 48][0];
+            }
+            rst += sh.xs[w];
+        }
+    } else if (wave == 0) {
         for (int w = 0; w < DEC_WAVES; w++) {
 #pragma unroll
             for (int i = 0; i < 4; i++)
@@ -580,13 +751,13 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         bool ok;
         const uint32_t tag = sh.u32[0];
         if (M <= 2)
-            ec_e = ec_consume<1>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<1, (GV && 1 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
         else if (M <= 4)
-            ec_e = ec_consume<2>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<2, (GV && 2 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
         else if (M <= 8)
-            ec_e = ec_consume<4>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<4, (GV && 4 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
         else
-            ec_e = ec_consume<8>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<8, (GV && 8 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
     }
     if (epi && wave == 0) {
         float yv[4];
@@ -655,11 +826,11 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
 }
 
 // Dynamic LDS beyond 64 KiB must be enabled per kernel once.
-template <int EC_MODE, int OUT_F32, int SW>
+template <int EC_MODE, int OUT_F32, int SW, int GV>
 hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
 {
     static const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_kernel<EC_MODE, OUT_F32, SW>),
+        reinterpret_cast<const void *>(&decode_kernel<EC_MODE, OUT_F32, SW, GV>),
         hipFuncAttributeMaxDynamicSharedMemorySize, DEC_LDS_MAX);
     if (e != hipSuccess)
         return e;
@@ -669,29 +840,40 @@ hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
     size_t lds = (size_t)(a.M + 1) * (size_t)(a.spw * 256 + 16);
     if (EC_MODE == 1 && lds < EC_LDS)
         lds = EC_LDS;                                     // EC partials meet in the same LDS
-    hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW, GV>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
-template <int EC_MODE, int OUT_F32>
+template <int EC_MODE, int OUT_F32, int GV>
 hipError_t launch_decode_sw(const LinearArgs &a, hipStream_t s)
 {
     switch ((a.spw + DEC_WAVES - 1) / DEC_WAVES) {
-    case 1: return launch_decode_k<EC_MODE, OUT_F32, 1>(a, s);
-    case 2: return launch_decode_k<EC_MODE, OUT_F32, 2>(a, s);
-    case 3: return launch_decode_k<EC_MODE, OUT_F32, 3>(a, s);
-    case 4: return launch_decode_k<EC_MODE, OUT_F32, 4>(a, s);
-    case 5: return launch_decode_k<EC_MODE, OUT_F32, 5>(a, s);
-    case 6: return launch_decode_k<EC_MODE, OUT_F32, 6>(a, s);
-    case 7: return launch_decode_k<EC_MODE, OUT_F32, 7>(a, s);
-    default: return launch_decode_k<EC_MODE, OUT_F32, 8>(a, s);
+    case 1: return launch_decode_k<EC_MODE, OUT_F32, 1, GV>(a, s);
+    case 2: return launch_decode_k<EC_MODE, OUT_F32, 2, GV>(a, s);
+    case 3: return launch_decode_k<EC_MODE, OUT_F32, 3, GV>(a, s);
+    case 4: return launch_decode_k<EC_MODE, OUT_F32, 4, GV>(a, s);
+    case 5: return launch_decode_k<EC_MODE, OUT_F32, 5, GV>(a, s);
+    case 6: return launch_decode_k<EC_MODE, OUT_F32, 6, GV>(a, s);
+    case 7: return launch_decode_k<EC_MODE, OUT_F32, 7, GV>(a, s);
+    default: return launch_decode_k<EC_MODE, OUT_F32, 8, GV>(a, s);
     }
+}
+
+// One token takes the GEMV form (vector ALU); 2..16 tokens share every
+// unpacked weight, a dense contraction, and take MFMA.  The pre-pass EC mode
+// keeps the MFMA form for every M.
+template <int EC_MODE, int OUT_F32>
+hipError_t launch_decode_gv(const LinearArgs &a, hipStream_t s)
+{
+    if (EC_MODE != 2 && a.M == 1)
+        return launch_decode_sw<EC_MODE, OUT_F32, (EC_MODE != 2 ? 1 : 0)>(a, s);
+    return launch_decode_sw<EC_MODE, OUT_F32, 0>(a, s);
 }
 
 template <int EC_MODE>
 hipError_t launch_decode_t(const LinearArgs &a, hipStream_t s)
 {
-    return a.out_f32 ? launch_decode_sw<EC_MODE, 1>(a, s) : launch_decode_sw<EC_MODE, 0>(a, s);
+    return a.out_f32 ? launch_decode_gv<EC_MODE, 1>(a, s) : launch_decode_gv<EC_MODE, 0>(a, s);
 }
 
 } // namespace
