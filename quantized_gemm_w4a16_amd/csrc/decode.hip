@@ -549,26 +549,30 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         }
     }
 
-    // 3. Activations of the K range -> LDS directly (global_load_lds, 16 bytes a
-    //    lane, 64 consecutive chunks of one token row per wave instruction).
-    //    Chunks past K and the extra row M (read by token slots >= M) are zeros.
+    // 3. Activations -> LDS directly (global_load_lds, 16 bytes a lane, 64
+    //    consecutive chunks of one token row per wave instruction).  Each wave
+    //    stages exactly the chunks of its own super-steps (the only ones it
+    //    reads), so no workgroup barrier separates staging from contraction.
+    //    Chunks past K and the wave's part of the extra row M (read by token
+    //    slots >= M) are zeros.
+    const int sl0 = wave * SW;                               // first local super-step
+    const int64_t c0 = 16 * (int64_t)sl0;                    // the wave's chunks [c0, c1)
+    const int64_t c1 = (c0 + 16 * SW < cpr) ? c0 + 16 * SW : cpr;
     if (stream) {
-        const int64_t npass = (cpr + DEC_THREADS - 1) / DEC_THREADS;
         for (int64_t m = 0; m < M; m++) {
-            for (int64_t ps = 0; ps < npass; ps++) {
-                const int64_t q0 = ps * DEC_THREADS + wave * 64;      // first chunk of this wave
+            for (int64_t q0 = c0; q0 < c1; q0 += 64) {
                 const int64_t q = q0 + lane;
                 const int64_t k = s_begin * 128 + 8 * q;
-                if (q0 < cpr && q < cpr && k < K)
+                if (q < c1 && k < K)
                     __builtin_amdgcn_global_load_lds(
                         (const __attribute__((address_space(1))) void *)(a.x + m * K + k),
                         (__attribute__((address_space(3))) void *)(s_x + m * rs_bytes + 16 * q0),
                         16, 0, 0);
-                else if (q < cpr)
+                else if (q < c1)
                     *reinterpret_cast<u32x4 *>(s_x + m * rs_bytes + 16 * q) = zero4();
             }
         }
-        for (int64_t q = tid; q < cpr; q += DEC_THREADS)
+        for (int64_t q = c0 + lane; q < c1; q += 64)
             *reinterpret_cast<u32x4 *>(s_x + M * rs_bytes + 16 * q) = zero4();
     }
 
@@ -576,7 +580,6 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     //    range rows and depths read clamped in-bounds addresses; their products
     //    meet zero activations or are never stored.
     u32x4 wr[SW];
-    const int sl0 = wave * SW;                               // first local super-step
 #pragma unroll
     for (int i = 0; i < SW; i++) {
         int64_t k = (s_begin + sl0 + i) * 128 + 32 * lg;
@@ -590,20 +593,20 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         claimed = epoch_claim(a);
 
     // Wait for everything but the weight stream (the SW youngest loads) and for
-    // the LDS zero fills, then make the activations visible to the workgroup.
-    // The weight loads stay in flight; each super-step waits for its own.  (In
-    // the wave that claimed the epoch the claim is the youngest operation, so
-    // there the first weight load is waited for too; it is needed next.)
+    // the LDS zero fills: the wave's activations are then in LDS.  The weight
+    // loads stay in flight; each super-step waits for its own.  (In the wave
+    // that claimed the epoch the claim is the youngest operation, so there the
+    // first weight load is waited for too; it is needed next.)
     wait_vmcnt<SW>();
     wait_lgkmcnt0();
-    bare_barrier();
 
-    // 5. Permute the activations in place to the unpack pair order, once.  One
-    //    token: also sum the activations of the range (each wave its chunks,
-    //    reduced across the wave in a fixed butterfly order).
+    // 5. One token: permute the wave's activations in place to the unpack pair
+    //    order (each chunk is read by all 16 channel lanes) and sum them, reduced
+    //    across the wave in a fixed butterfly order.  More tokens permute in
+    //    registers as they read (each chunk is read by one lane).
     if (GV) {
         float xsum = 0.f;
-        for (int64_t q = tid; q < cpr; q += DEC_THREADS) {
+        for (int64_t q = c0 + lane; q < c1; q += 64) {
             u32x4 *p = reinterpret_cast<u32x4 *>(s_x + 16 * q);
             const u32x4 v = *p;
             xsum = sum8(v, xsum);
@@ -614,16 +617,8 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
             xsum += __shfl_xor(xsum, o);
         if (lane == 0)
             sh.xs[wave] = xsum;
-    } else {
-        for (int64_t m = 0; m < M; m++) {
-            for (int64_t q = tid; q < cpr; q += DEC_THREADS) {
-                u32x4 *p = reinterpret_cast<u32x4 *>(s_x + m * rs_bytes + 16 * q);
-                *p = perm8(*p);
-            }
-        }
+        wait_lgkmcnt0();
     }
-    wait_lgkmcnt0();
-    bare_barrier();
 
     // 6. Contraction (stream waves), each super-step as soon as its weights land.
     if (GV) {
@@ -662,7 +657,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
                 u32x4 xr[4];
 #pragma unroll
                 for (int d = 0; d < 4; d++)
-                    xr[d] = *reinterpret_cast<const u32x4 *>(xrow + (16 * sl + 4 * lg + d) * 16);
+                    xr[d] = perm8(*reinterpret_cast<const u32x4 *>(xrow + (16 * sl + 4 * lg + d) * 16));
                 acc0 = mfma16(unpack8(wr[i][0]), xr[0], acc0);
                 rs0 = mfma16(ones, xr[0], rs0);
                 acc1 = mfma16(unpack8(wr[i][1]), xr[1], acc1);
