@@ -20,6 +20,7 @@ TFLOP/s); it is not the default line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -48,6 +49,23 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for counter scaling)")
     return p.parse_args()
+
+
+def profiled_traffic():
+    """HBM bytes per fused decode launch from the committed rocprofv3 counter
+    record (FETCH_SIZE + WRITE_SIZE, calibrated on a device copy), or None when
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "decode_fused_c2_hbm_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for name in ("decode.hip", "api.hip", "spear_internal.hpp"):
+        with open(os.path.join(ROOT, "quantized_gemm_w4a16_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return rec.get("traffic_bytes_per_launch") if h.hexdigest() == rec.get("source_sha256") else None
 
 
 def dev(a, torch):
@@ -197,8 +215,10 @@ def run_c2(args, torch, sp, gen):
         "plain_GBps": round(per_step_plain / (t_plain / args.steps * 1e-3) / 1e9, 2),
         "us_per_launch": round(ms_step / launches * 1e3, 3),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel<1,1> (fused EC, fp32 out)",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(),
+                     "traffic_unit": "bytes per launch (profiles/decode_fused_c2_hbm_traffic.md)",
+                     "kernel": "decode_kernel<1,1,*,*> (fused EC, fp32 out)",
                      "bytes_per_launch": round(per_step_bytes / launches)},
     }
     return out
