@@ -81,6 +81,8 @@ typedef int32_t spear_status;
 #define SPEAR_PATH_PREFILL       2 /* any M: EC pre-pass, then the MFMA GEMM whose
                                       epilogue applies the EC                           */
 #define SPEAR_PATH_DECODE_2PASS  3 /* M <= 16: EC pre-pass, then the decode kernel      */
+#define SPEAR_PATH_PREFILL_LARGE 4 /* any M: EC pre-pass, then the 256 x 128-tile MFMA
+                                      GEMM (the prefill path's choice for large M)     */
 
 /* Largest EC rank accepted; the rank must also be a multiple of 8. */
 #define SPEAR_MAX_RANK 256
@@ -111,8 +113,12 @@ typedef struct spear_ec {
 /*
  * spear_pack_w4 -- pack 4-bit codes for spear_w4_linear.
  *   codes     [N][K] int8 (SPEAR_CODES_S4) or uint8 (SPEAR_CODES_U4); 16-byte aligned.
- *   packed    [N][K/2] output; byte [n][i] holds u[n][2i] in bits 0-3 and
- *             u[n][2i+1] in bits 4-7 (u = q + 8 for signed codes).  16-byte aligned.
+ *   packed    [N][K/2] output, 16-byte aligned: each row is a run of little-endian
+ *             32-bit words, word w holding u[n][8w .. 8w+7]; nibble position p
+ *             (bits 4p .. 4p+3) holds u[n][8w + perm[p]], perm = (0,2,4,6,1,3,5,7):
+ *             byte 0 holds codes 0 and 2 (low, high nibble), byte 1 codes 4 and 6,
+ *             byte 2 codes 1 and 3, byte 3 codes 5 and 7 (u = q + 8 for signed
+ *             codes).  A shift and a mask then give bf16 pairs in natural order.
  *   bad_codes optional device int32 counter; the number of out-of-range codes is
  *             ADDED to it.  Out-of-range codes are packed as their low 4 bits.
  * Shapes: N >= 1, K >= 32, K % 32 == 0.  Source: the summary's section 3.1

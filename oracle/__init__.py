@@ -77,13 +77,14 @@ def pack_w4(codes: np.ndarray, kind: int):
     dt = np.int8 if kind == CODES_S4 else np.uint8
     codes = _c(codes, dt)
     N, K = codes.shape
-    assert K % 2 == 0
+    assert K % 8 == 0, "the packed layout works in words of 8 codes"
     out = np.empty((N, K // 2), dtype=np.uint8)
     bad = _load().oracle_pack_w4(_ptr(codes), kind, N, K, _ptr(out))
     return out, int(bad)
 
 
 def unpack_w4(packed: np.ndarray, K: int) -> np.ndarray:
+    assert K % 8 == 0, "the packed layout works in words of 8 codes"
     packed = _c(packed, np.uint8)
     N = packed.shape[0]
     out = np.empty((N, K), dtype=np.uint8)

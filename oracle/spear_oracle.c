@@ -30,8 +30,9 @@
  *   - Codes: signed codes q in [-8,7] are stored offset-binary u = q + 8 with
  *     zero point 8; unsigned codes u in [0,15] carry a per-channel zero point.
  *     Dequantised weight w = s_n * (u - z_n).
- *   - Packed layout: byte [n][i] holds u[n][2i] in its low nibble and
- *     u[n][2i+1] in its high nibble.
+ *   - Packed layout (see nibble_index): rows of little-endian 32-bit words
+ *     of 8 codes, nibble position p of a word holding code perm[p],
+ *     perm = (0, 2, 4, 6, 1, 3, 5, 7).
  *
  * Precision: dequantised weights are formed in fp32 (s_n * (u - z_n)
  * evaluated in float); every sum (the main contraction, the gate logit, the
@@ -82,14 +83,29 @@ static uint8_t code_to_nibble(const void *codes, int kind, int64_t i, int64_t *b
     }
 }
 
+/* Packed layout (this library's; the pages give none): each row is a run of
+ * 32-bit little-endian words, word w holding codes k = 8w .. 8w+7.  Nibble
+ * position p of the word (bits 4p .. 4p+3) holds code 8w + perm[p] with
+ * perm = (0, 2, 4, 6, 1, 3, 5, 7): byte 0 holds codes 0 and 2 (low, high
+ * nibble), byte 1 codes 4 and 6, byte 2 codes 1 and 3, byte 3 codes 5 and 7.
+ * The nibble position of code 8w + i is therefore i / 2 for even i and
+ * 4 + i / 2 for odd i. */
+static int64_t nibble_index(int64_t K, int64_t n, int64_t k)
+{
+    const int64_t w = k / 8, i = k % 8;
+    const int64_t p = (i % 2 == 0) ? i / 2 : 4 + i / 2;
+    return (n * (K / 2) + 4 * w) * 2 + p;          /* byte = index / 2, high nibble if odd */
+}
+
 int64_t oracle_pack_w4(const void *codes, int kind, int64_t N, int64_t K, uint8_t *packed)
 {
     int64_t bad = 0;
+    memset(packed, 0, (size_t)(N * (K / 2)));
     for (int64_t n = 0; n < N; n++) {
-        for (int64_t i = 0; i < K / 2; i++) {
-            uint8_t lo = code_to_nibble(codes, kind, n * K + 2 * i, &bad);
-            uint8_t hi = code_to_nibble(codes, kind, n * K + 2 * i + 1, &bad);
-            packed[n * (K / 2) + i] = (uint8_t)(lo | (hi << 4));
+        for (int64_t k = 0; k < K; k++) {
+            const uint8_t u = code_to_nibble(codes, kind, n * K + k, &bad);
+            const int64_t q = nibble_index(K, n, k);
+            packed[q / 2] |= (uint8_t)((q % 2) ? (u << 4) : u);
         }
     }
     return bad;
@@ -98,8 +114,9 @@ int64_t oracle_pack_w4(const void *codes, int kind, int64_t N, int64_t K, uint8_
 /* Scalar unpack of one nibble. */
 static int nibble_at(const uint8_t *packed, int64_t K, int64_t n, int64_t k)
 {
-    uint8_t byte = packed[n * (K / 2) + k / 2];
-    return (k & 1) ? (byte >> 4) : (byte & 0xF);
+    const int64_t q = nibble_index(K, n, k);
+    const uint8_t byte = packed[q / 2];
+    return (q % 2) ? (byte >> 4) : (byte & 0xF);
 }
 
 void oracle_unpack_w4(const uint8_t *packed, int64_t N, int64_t K, uint8_t *u)

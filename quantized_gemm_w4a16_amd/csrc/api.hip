@@ -61,6 +61,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
     off = align256(off + HDR_WORDS * sizeof(uint32_t));
     L.epoch = off;
     off = align256(off + (size_t)EPOCH_CTRS * EPOCH_STRIDE);
+    L.zeros = off;                                        // 256 bytes that stay zero: DMA source
+    off = align256(off + 256);
     L.colcnt = off;
     off = align256(off + (size_t)L.ncg * sizeof(uint32_t));
     L.splitp = off;
@@ -250,7 +252,7 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
         return SPEAR_E_SHAPE;
     if (ec && (ec->r < 8 || ec->r > SPEAR_MAX_RANK || ec->r % 8 != 0))
         return SPEAR_E_SHAPE;
-    if (path < SPEAR_PATH_AUTO || path > SPEAR_PATH_DECODE_2PASS)
+    if (path < SPEAR_PATH_AUTO || path > SPEAR_PATH_PREFILL_LARGE)
         return SPEAR_E_ARG;
     if (out_dtype != SPEAR_OUT_BF16 && out_dtype != SPEAR_OUT_F32)
         return SPEAR_E_ARG;
@@ -340,7 +342,7 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
                 e = launch_compact(active, M, a.idx_out, a.nact_out, s);
         }
         if (e == hipSuccess)
-            e = launch_gemm(a, ec ? 1 : 0, s);
+            e = launch_gemm(a, ec ? 1 : 0, path == SPEAR_PATH_PREFILL_LARGE, s);
         break;
     }
     return hip_status(e);

@@ -13,9 +13,9 @@
 //    activations of the range would not fit in LDS).  Its 4 stream waves load
 //    the activations of the range straight into LDS (global_load_lds), then
 //    issue every 16-byte load of their packed-weight share (HBM -> registers)
-//    and contract on bf16 MFMA as each load lands (activations permuted to the
-//    unpack order in LDS), with the tokens (padded to 16) as the MFMA's N
-//    side.  A second MFMA against a constant-one operand gives the per-token
+//    and contract on bf16 MFMA as each load lands (the packed word order makes
+//    the unpacked pairs line up with the activations' own pairs), with the
+//    tokens (padded to 16) as the MFMA's N side.  A second MFMA against a constant-one operand gives the per-token
 //    activation sums that remove the unpack offset in the epilogue.
 //  * When K is split over workgroups, the last one of a channel group (atomic
 //    counter) sums the partial tiles in slice order (deterministic).
@@ -600,32 +600,26 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     wait_vmcnt<SW>();
     wait_lgkmcnt0();
 
-    // 5. One token: permute the wave's activations in place to the unpack pair
-    //    order (each chunk is read by all 16 channel lanes) and sum them, reduced
-    //    across the wave in a fixed butterfly order.  More tokens permute in
-    //    registers as they read (each chunk is read by one lane).
+    // 5. One token: sum the wave's activations (the offset removal needs the
+    //    token's activation sum), reduced across the wave in a fixed butterfly
+    //    order.  More tokens take their sums from a ones-MFMA in the loop.
     if (GV) {
         float xsum = 0.f;
-        for (int64_t q = c0 + lane; q < c1; q += 64) {
-            u32x4 *p = reinterpret_cast<u32x4 *>(s_x + 16 * q);
-            const u32x4 v = *p;
-            xsum = sum8(v, xsum);
-            *p = perm8(v);
-        }
+        for (int64_t q = c0 + lane; q < c1; q += 64)
+            xsum = sum8(*reinterpret_cast<const u32x4 *>(s_x + 16 * q), xsum);
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1)
             xsum += __shfl_xor(xsum, o);
         if (lane == 0)
             sh.xs[wave] = xsum;
-        wait_lgkmcnt0();
     }
 
     // 6. Contraction (stream waves), each super-step as soon as its weights land.
     if (GV) {
         // One token: a wavefront-reduction GEMV.  Lane (c, g) holds channel
         // n0 + c and 32 consecutive k of each super-step; the unpacked pairs
-        // meet the permuted activation pairs in bf16 dot2 (fp32), one
-        // accumulator per 8-deep quarter.
+        // meet the activation pairs in bf16 dot2 (fp32), one accumulator per
+        // 8-deep quarter.
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < SW; i++) {
@@ -657,7 +651,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
                 u32x4 xr[4];
 #pragma unroll
                 for (int d = 0; d < 4; d++)
-                    xr[d] = perm8(*reinterpret_cast<const u32x4 *>(xrow + (16 * sl + 4 * lg + d) * 16));
+                    xr[d] = *reinterpret_cast<const u32x4 *>(xrow + (16 * sl + 4 * lg + d) * 16);
                 acc0 = mfma16(unpack8(wr[i][0]), xr[0], acc0);
                 rs0 = mfma16(ones, xr[0], rs0);
                 acc1 = mfma16(unpack8(wr[i][1]), xr[1], acc1);

@@ -10,8 +10,10 @@
 namespace spear {
 
 // ------------------------------------------------------------------- packing
-// One thread: 16 codes (one 16-byte load) -> 8 packed bytes.  Signed codes are
-// stored offset-binary: the low nibble of q + 8 is (q & 15) ^ 8.
+// One thread: 16 codes (one 16-byte load) -> 8 packed bytes, two words of 8
+// codes.  Signed codes are stored offset-binary: the low nibble of q + 8 is
+// (q & 15) ^ 8.  Word layout: byte 0 holds codes 0 and 2 (low, high nibble),
+// byte 1 codes 4 and 6, byte 2 codes 1 and 3, byte 3 codes 5 and 7.
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ codes,
                                                    int32_t kind, int64_t nchunks,
                                                    uint8_t *__restrict__ packed,
@@ -23,6 +25,7 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
     const u32x4 c = ld16(codes + 16 * i);
     uint32_t out[2];
     int nbad = 0;
+    uint32_t u[4];
 #pragma unroll
     for (int d = 0; d < 4; d++) {
         const uint32_t v = c[d];
@@ -31,15 +34,18 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ c
             const uint32_t byte = (v >> (8 * j)) & 0xFFu;
             nbad += kind == SPEAR_CODES_S4 ? (((byte + 8u) & 0xFFu) > 15u) : (byte > 15u);
         }
-        uint32_t u = v & 0x0F0F0F0Fu;
+        u[d] = v & 0x0F0F0F0Fu;
         if (kind == SPEAR_CODES_S4)
-            u ^= 0x08080808u;
-        const uint32_t t = u | (u >> 4);                    // bytes 0 and 2 hold the pairs
-        const uint32_t h = (t & 0xFFu) | ((t >> 8) & 0xFF00u);
-        if (d & 1)
-            out[d >> 1] |= h << 16;
-        else
-            out[d >> 1] = h;
+            u[d] ^= 0x08080808u;
+    }
+#pragma unroll
+    for (int w = 0; w < 2; w++) {
+        // a holds codes 0..3 of the word (one per byte), b codes 4..7; a | a >> 12
+        // has codes 0 | 2 << 4 in byte 0 and codes 1 | 3 << 4 in byte 1.
+        const uint32_t a = u[2 * w], b = u[2 * w + 1];
+        const uint32_t ta = a | (a >> 12), tb = b | (b >> 12);
+        out[w] = (ta & 0xFFu) | ((tb & 0xFFu) << 8) | (((ta >> 8) & 0xFFu) << 16) |
+                 (((tb >> 8) & 0xFFu) << 24);
     }
     uint2 o;
     o.x = out[0];

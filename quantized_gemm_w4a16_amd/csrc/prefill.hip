@@ -110,9 +110,8 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
 // 4 consecutive channels of one token (contiguous stores).  K advances in
 // 128-deep super-steps.  Packed weights: HBM -> registers (16-byte loads, one
 // super-step of prefetch), unpacked to bf16 (1 + u/16) pairs in registers.
-// Activations: HBM -> registers -> LDS (double-buffered), permuted on the way
-// to match the unpacked pair order, and summed per token for the epilogue's
-// offset removal.  Epilogue: y = s_n (16 acc - (16 + z_n) sum_k x) + B v.
+// Activations: HBM -> registers -> LDS (double-buffered), summed per token on
+// the way for the epilogue's offset removal.  Epilogue: y = s_n (16 acc - (16 + z_n) sum_k x) + B v.
 template <int FN, int FM, int WNW, int WMW, int EC, int OUT_F32>
 __global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a)
 {
@@ -191,7 +190,7 @@ __global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a
         for (int i = 0; i < CPT; i++) {
             const int row = srow0 + (NT / 16) * i;
             rsp[i] = sum8(xs[i], rsp[i]);
-            *reinterpret_cast<u32x4 *>(&s_x[buf][row * RS + 16 * sc]) = perm8(xs[i]);
+            *reinterpret_cast<u32x4 *>(&s_x[buf][row * RS + 16 * sc]) = xs[i];
         }
     };
 
@@ -348,6 +347,291 @@ hipError_t launch_gemm_t(const LinearArgs &a, int ec_on, hipStream_t s)
     return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------- large-M GEMM
+// Output tile 256 channels x 128 tokens, 8 waves (4 along the channels x 2
+// along the tokens), each 64 x 64 as 4 x 4 MFMA tiles.  K advances in stages
+// of 128.  Both operands go HBM/L2 -> LDS by global_load_lds into a ring of
+// G2_STAGES stage buffers, so the only memory operations in flight are these
+// DMAs: one stage is read while the next ones land.  Each wave waits for its
+// own part of a stage (vmcnt) and one barrier per stage makes every part
+// visible.  The stage buffers are separate LDS objects and nothing but the
+// DMAs writes them, so the compiler can tell that reading one stage does not
+// depend on the DMAs into the others and does not wait for them.
+// Layouts are XOR-swizzled on the global side so the rows one MFMA operand
+// reads fall in distinct banks: activation rows (256 bytes of bf16) swap their
+// 16-byte chunks by row % 16, weight rows (64 bytes of nibbles) by
+// (row / 2) % 4.  Weights are unpacked as they leave LDS (the packed word
+// order makes the unpacked pairs line up with the activations' own pairs).
+// Chunks past K are DMA'd from a zero block of the workspace.  The per-token
+// activation sums of the offset removal come from one extra MFMA against a
+// constant-one operand per token fragment: wave column c takes the 8-deep
+// quarter c of every 32-deep step, so the extra work is spread evenly.
+constexpr int G2_WN = 4, G2_WM = 2, G2_FN = 4, G2_FM = 4;
+constexpr int G2_NT = 64 * G2_WN * G2_WM;                 // 512 threads
+constexpr int G2_BN = 16 * G2_FN * G2_WN;                 // 256 channels
+constexpr int G2_BM = 16 * G2_FM * G2_WM;                 // 128 tokens
+constexpr int G2_STAGES = 3;
+constexpr int G2_XB = G2_BM * 256;                        // activation bytes of one stage
+constexpr int G2_WB = G2_BN * 64;                         // packed weight bytes of one stage
+constexpr int G2_XI = G2_XB / (G2_NT * 16);               // activation DMAs a lane, per stage
+constexpr int G2_WI = G2_WB / (G2_NT * 16);               // weight DMAs a lane, per stage
+static_assert(G2_XI * G2_NT * 16 == G2_XB && G2_WI * G2_NT * 16 == G2_WB, "stage split");
+
+// LDS byte offsets: chunk c (0..15) of activation row r, chunk c (0..3) of weight row r.
+__device__ __forceinline__ uint32_t g2_xoff(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
+__device__ __forceinline__ uint32_t g2_woff(int r, int c) { return r * 64 + ((c ^ ((r >> 1) & 3)) << 4); }
+
+// Four 16-byte LDS reads.
+__device__ __forceinline__ void lds_read4(const uint8_t *base, uint32_t a0, uint32_t a1, uint32_t a2,
+                                          uint32_t a3, u32x4 &r0, u32x4 &r1, u32x4 &r2, u32x4 &r3)
+{
+    r0 = *reinterpret_cast<const u32x4 *>(base + a0);
+    r1 = *reinterpret_cast<const u32x4 *>(base + a1);
+    r2 = *reinterpret_cast<const u32x4 *>(base + a2);
+    r3 = *reinterpret_cast<const u32x4 *>(base + a3);
+}
+
+template <int EC, int OUT_F32>
+__global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t s_x0[G2_XB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x1[G2_XB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x2[G2_XB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w0[G2_WB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w1[G2_WB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w2[G2_WB];
+    __shared__ float s_rsp[G2_WN][G2_BM];     // activation-sum quarters
+    static_assert(G2_STAGES == 3, "one LDS object per stage");
+    static_assert(G2_WN == 4, "one 8-deep quarter per wave column");
+    uint8_t *const s_xb[G2_STAGES] = {s_x0, s_x1, s_x2};
+    uint8_t *const s_wb[G2_STAGES] = {s_w0, s_w1, s_w2};
+
+    pin_args(a);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+    const int lr = lane & 15, lg = lane >> 4;
+    const int wn = wave % G2_WN, wm = wave / G2_WN;
+    const int64_t M = a.M, N = a.N, K = a.K;
+    const int64_t tiles_n = (N + G2_BN - 1) / G2_BN, tiles_m = (M + G2_BM - 1) / G2_BM;
+    const int64_t ntiles = tiles_n * tiles_m;
+
+    // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
+    // of tiles (channels fastest) so its L2 shares activation rows and weights.
+    const int64_t bid = blockIdx.x;
+    const int64_t q8 = ntiles / 8, r8 = ntiles % 8;
+    const int64_t xcd = bid % 8, loc = bid / 8;
+    const int64_t tile = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
+    const int64_t n0 = (tile % tiles_n) * G2_BN, m0 = (tile / tiles_n) * G2_BM;
+    const int64_t S = (K + 127) / 128;
+    const uint8_t *zsrc = a.ws + a.L.zeros + 16 * (lane & 15);
+
+    // DMA of one stage.  Activations: instruction j of wave w fills rows
+    // 4 (G2_XI w + j) .. +3, lane i the slot i of that 1 KB (chunk (i % 16) ^
+    // (row % 16) of its row); rows past M repeat row M - 1 (never stored).
+    // Weights: instruction j fills rows 16 (G2_WI w + j) .. +15, lane i the slot
+    // i of that 1 KB (chunk (i % 4) ^ ((row / 2) % 4)); rows past N repeat the
+    // last row.
+    auto issue = [&](int64_t st, uint8_t *xbase, uint8_t *wbase) {
+#pragma unroll
+        for (int j = 0; j < G2_XI; j++) {
+            const int r0 = 4 * (G2_XI * wave + j);
+            const int r = r0 + (lane >> 4);
+            const int c = (lane & 15) ^ (r & 15);
+            const int64_t k = 128 * st + 8 * c;
+            int64_t mm = m0 + r;
+            mm = mm < M ? mm : M - 1;
+            const void *src = (k < K) ? (const void *)(a.x + mm * K + k) : (const void *)zsrc;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(xbase + r0 * 256),
+                                             16, 0, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < G2_WI; j++) {
+            const int r0 = 16 * (G2_WI * wave + j);
+            const int r = r0 + (lane >> 2);
+            const int c = (lane & 3) ^ ((r >> 1) & 3);
+            const int64_t k = 128 * st + 32 * c;
+            int64_t nn = n0 + r;
+            nn = nn < N ? nn : N - 1;
+            const void *src = (k < K) ? (const void *)(a.packed + nn * (K / 2) + k / 2)
+                                      : (const void *)zsrc;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                             (__attribute__((address_space(3))) void *)(wbase + r0 * 64),
+                                             16, 0, 0);
+        }
+    };
+
+    f32x4 acc[G2_FN][G2_FM], rsq[G2_FM];
+    const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+#pragma unroll
+    for (int fn = 0; fn < G2_FN; fn++)
+#pragma unroll
+        for (int fm = 0; fm < G2_FM; fm++)
+            acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int fm = 0; fm < G2_FM; fm++)
+        rsq[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // LDS addresses this lane reads (stage-relative).
+    uint32_t xoff[4][G2_FM], woff[G2_FN];
+#pragma unroll
+    for (int d = 0; d < 4; d++)
+#pragma unroll
+        for (int fm = 0; fm < G2_FM; fm++)
+            xoff[d][fm] = g2_xoff((wm * G2_FM + fm) * 16 + lr, 4 * lg + d);
+#pragma unroll
+    for (int fn = 0; fn < G2_FN; fn++)
+        woff[fn] = g2_woff((wn * G2_FN + fn) * 16 + lr, lg);
+
+    // Every stage slot issues its DMAs, past the end clamped to the last stage
+    // (never used), so each wave always has exactly one further stage in flight
+    // when it waits for the current one.
+    const int64_t slast = S - 1;
+#pragma unroll
+    for (int j = 0; j < G2_STAGES - 1; j++)
+        issue(j < slast ? j : slast, s_xb[j], s_wb[j]);
+    constexpr int G2_WAIT = (G2_XI + G2_WI) * (G2_STAGES - 2);
+    static_assert(G2_WAIT < 64, "vmcnt");
+
+    for (int64_t s0 = 0; s0 < S; s0 += G2_STAGES) {
+#pragma unroll
+        for (int j = 0; j < G2_STAGES; j++) {
+            const int64_t s = s0 + j;
+            wait_vmcnt<G2_WAIT>();                            // this wave's part of stage s
+            bare_barrier();                                   // every wave's part; stage s - 1 free
+            const int64_t sn = (s + G2_STAGES - 1 < slast) ? s + G2_STAGES - 1 : slast;
+            issue(sn, s_xb[(j + G2_STAGES - 1) % G2_STAGES], s_wb[(j + G2_STAGES - 1) % G2_STAGES]);
+            if (s < S) {
+                const uint8_t *xb = s_xb[j], *wb = s_wb[j];
+                u32x4 wv[G2_FN];
+                lds_read4(wb, woff[0], woff[1], woff[2], woff[3], wv[0], wv[1], wv[2], wv[3]);
+#pragma unroll
+                for (int d = 0; d < 4; d++) {
+                    u32x4 xf[G2_FM];
+                    lds_read4(xb, xoff[d][0], xoff[d][1], xoff[d][2], xoff[d][3],
+                              xf[0], xf[1], xf[2], xf[3]);
+                    if (d == wn) {
+#pragma unroll
+                        for (int fm = 0; fm < G2_FM; fm++)
+                            rsq[fm] = mfma16(ones, xf[fm], rsq[fm]);
+                    }
+#pragma unroll
+                    for (int fn = 0; fn < G2_FN; fn++) {
+                        const u32x4 wa = unpack8(wv[fn][d]);
+#pragma unroll
+                        for (int fm = 0; fm < G2_FM; fm++)
+                            acc[fn][fm] = mfma16(wa, xf[fm], acc[fn][fm]);
+                    }
+                }
+            }
+        }
+    }
+    wait_vmcnt<0>();                                          // the clamped tail DMAs
+
+    // Per-token activation sums: this wave column's quarter (every output row of
+    // the ones-MFMA holds the same sum), then the four quarters in order.
+    if (lg == 0) {
+#pragma unroll
+        for (int fm = 0; fm < G2_FM; fm++)
+            s_rsp[wn][(wm * G2_FM + fm) * 16 + lr] = rsq[fm][0];
+    }
+    __syncthreads();
+
+    // Epilogue: scale and offset removal, the EC term, store.
+#pragma unroll
+    for (int fn = 0; fn < G2_FN; fn++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int64_t nn = n0 + (wn * G2_FN + fn) * 16 + 4 * lg + i;
+            nn = nn < N ? nn : N - 1;
+            const float sn = a.scales[nn];
+            const float zc = UNPACK_OFF + zero_point(a.zeros, load_zero_byte(a.zeros, a.scales, nn));
+#pragma unroll
+            for (int fm = 0; fm < G2_FM; fm++) {
+                const int row = (wm * G2_FM + fm) * 16 + lr;
+                const float rsm = ((s_rsp[0][row] + s_rsp[1][row]) + s_rsp[2][row]) + s_rsp[3][row];
+                acc[fn][fm][i] = sn * __builtin_fmaf(-zc, rsm, UNPACK_SCALE * acc[fn][fm][i]);
+            }
+        }
+    }
+    if (EC) {
+        const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
+        const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
+        const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
+        int any = 0;
+#pragma unroll
+        for (int fm = 0; fm < G2_FM; fm++) {
+            const int64_t mm = m0 + (wm * G2_FM + fm) * 16 + lr;
+            any |= (mm < M) ? active[mm] : 0;
+        }
+        if (__ballot(any) != 0ull) {
+            const int rpad = a.rpad, r = a.r;
+            for (int t = 0; t < rpad / 32; t++) {
+                const int j = 32 * t + 8 * lg;
+                u32x4 vh[G2_FM], vl[G2_FM];
+#pragma unroll
+                for (int fm = 0; fm < G2_FM; fm++) {
+                    const int64_t mm = m0 + (wm * G2_FM + fm) * 16 + lr;
+                    vh[fm] = (mm < M) ? ld16(vhi + mm * rpad + j) : zero4();
+                    vl[fm] = (mm < M) ? ld16(vlo + mm * rpad + j) : zero4();
+                }
+#pragma unroll
+                for (int fn = 0; fn < G2_FN; fn++) {
+                    const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
+                    const u32x4 bf = (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
+#pragma unroll
+                    for (int fm = 0; fm < G2_FM; fm++) {
+                        acc[fn][fm] = mfma16(bf, vh[fm], acc[fn][fm]);
+                        acc[fn][fm] = mfma16(bf, vl[fm], acc[fn][fm]);
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int fm = 0; fm < G2_FM; fm++) {
+        const int64_t mm = m0 + (wm * G2_FM + fm) * 16 + lr;
+        if (mm >= M)
+            continue;
+#pragma unroll
+        for (int fn = 0; fn < G2_FN; fn++) {
+            const int64_t nb = n0 + (wn * G2_FN + fn) * 16 + 4 * lg;
+            const f32x4 v = acc[fn][fm];
+            if (OUT_F32) {
+                float *y = reinterpret_cast<float *>(a.y) + mm * N;
+                if (nb + 3 < N && (N & 3) == 0) {
+                    *reinterpret_cast<f32x4 *>(y + nb) = v;
+                } else {
+                    for (int i = 0; i < 4; i++)
+                        if (nb + i < N)
+                            y[nb + i] = v[i];
+                }
+            } else {
+                uint16_t *y = reinterpret_cast<uint16_t *>(a.y) + mm * N;
+                if (nb + 3 < N && (N & 3) == 0) {
+                    uint2 o;
+                    o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+                    o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+                    *reinterpret_cast<uint2 *>(y + nb) = o;
+                } else {
+                    for (int i = 0; i < 4; i++)
+                        if (nb + i < N)
+                            y[nb + i] = f2bf(v[i]);
+                }
+            }
+        }
+    }
+}
+
+template <int EC, int OUT_F32>
+hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
+{
+    const int64_t ntiles = ((a.N + G2_BN - 1) / G2_BN) * ((a.M + G2_BM - 1) / G2_BM);
+    hipLaunchKernelGGL((gemm2_kernel<EC, OUT_F32>), dim3((unsigned)ntiles), dim3(G2_NT), 0, s, a);
+    return hipGetLastError();
+}
+
 } // namespace
 
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
@@ -357,11 +641,15 @@ hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const LinearArgs &a, int ec_on, hipStream_t s)
+hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStream_t s)
 {
-    if (a.M <= 64)
+    if (!force_large && a.M <= 64)
         return launch_gemm_t<2, 2, 2, 2>(a, ec_on, s);   // 64 x 64 tiles
-    return launch_gemm_t<4, 4, 2, 2>(a, ec_on, s);       // 128 x 128 tiles
+    if (!force_large && a.M * a.N < 256 * 128 * 256)     // too few 256 x 128 tiles to fill the chip
+        return launch_gemm_t<4, 4, 2, 2>(a, ec_on, s);   // 128 x 128 tiles
+    if (ec_on)
+        return a.out_f32 ? launch_gemm2_t<1, 1>(a, s) : launch_gemm2_t<1, 0>(a, s);
+    return a.out_f32 ? launch_gemm2_t<0, 1>(a, s) : launch_gemm2_t<0, 0>(a, s);
 }
 
 } // namespace spear

@@ -27,10 +27,11 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c)
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// 8 packed nibbles (depth positions 0..7, position i in bits 4i..4i+3) ->
-// bf16 pairs holding 1 + u/16 exactly: the nibble becomes the top 4 of the 7
-// mantissa bits of a value in [1, 2).  Pair p carries positions (p, p + 4):
-// (0,4) (1,5) (2,6) (3,7).  The epilogue removes the offset and the zero point:
+// One packed word (8 codes; nibble position p holds code (0,2,4,6,1,3,5,7)[p])
+// -> bf16 pairs holding 1 + u/16 exactly: the nibble becomes the top 4 of the 7
+// mantissa bits of a value in [1, 2).  Pair p takes nibble positions (p, p + 4),
+// i.e. codes (2p, 2p + 1): the pairs come out in natural order, as the
+// activations' bf16 pairs lie.  The epilogue removes the offset and the zero point:
 // 16 sum x (1 + u/16) - (16 + z) sum x = sum x (u - z).  Keeping the nibble in
 // the high mantissa bits keeps that offset small (16 sum x).
 __device__ __forceinline__ u32x4 unpack8(uint32_t w)
@@ -51,18 +52,6 @@ __device__ __forceinline__ u32x4 unpack8(uint32_t w)
 // Scale of the unpacked value and the offset it carries: unpacked = (OFF + u) / SCALE.
 constexpr float UNPACK_SCALE = 16.0f;
 constexpr float UNPACK_OFF = 16.0f;
-
-// 8 bf16 in natural order (pairs (0,1) (2,3) (4,5) (6,7)) -> the pair order
-// unpack8 produces: (0,4) (1,5) (2,6) (3,7).
-__device__ __forceinline__ u32x4 perm8(u32x4 d)
-{
-    u32x4 o;
-    o[0] = __builtin_amdgcn_perm(d[2], d[0], 0x05040100u);
-    o[1] = __builtin_amdgcn_perm(d[2], d[0], 0x07060302u);
-    o[2] = __builtin_amdgcn_perm(d[3], d[1], 0x05040100u);
-    o[3] = __builtin_amdgcn_perm(d[3], d[1], 0x07060302u);
-    return o;
-}
 
 __device__ __forceinline__ u32x4 ld16(const void *p)
 {
@@ -160,7 +149,7 @@ constexpr int MAX_PROD = 32;      // at most this many EC producer workgroups
 constexpr int PROD_CHUNK = 4;     // producer partials a consumer wave loads per batch
 
 struct WsLayout {
-    size_t hdr, epoch, colcnt, splitp, pu, pz, vhi, vlo, active, total;
+    size_t hdr, epoch, zeros, colcnt, splitp, pu, pz, vhi, vlo, active, total;
     int64_t ncg, ksplit, spw, nprod, prod_k, rpad, mpad;
 };
 
@@ -221,7 +210,7 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.idx_out); pin_arg(a.nact_out); pin_arg(a.thr); pin_arg(a.b); pin_arg(a.hard);
     pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
     pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
-    pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.colcnt); pin_arg(a.L.splitp); pin_arg(a.L.pu);
+    pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.colcnt); pin_arg(a.L.splitp); pin_arg(a.L.pu);
     pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);
 }
@@ -236,6 +225,6 @@ hipError_t launch_compact(const int32_t *flags, int64_t M, int32_t *idx, int32_t
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_decode(const LinearArgs &a, int ec_mode, hipStream_t s);
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s);
-hipError_t launch_gemm(const LinearArgs &a, int ec_on, hipStream_t s);
+hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStream_t s);
 
 } // namespace spear

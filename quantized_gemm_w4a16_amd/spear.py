@@ -26,6 +26,7 @@ PATH_AUTO = 0
 PATH_DECODE = 1
 PATH_PREFILL = 2
 PATH_DECODE_2PASS = 3
+PATH_PREFILL_LARGE = 4
 MAX_RANK = 256
 
 EXPORTS = ("spear_pack_w4", "spear_gate", "spear_w4_linear_workspace_size",

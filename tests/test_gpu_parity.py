@@ -16,7 +16,7 @@ from gpu_util import (assert_close, dev, errors, gpu_ec, gpu_weights, host, run_
 
 pytestmark = pytest.mark.gpu
 
-ALL_PATHS_SMALL = [sp.PATH_DECODE, sp.PATH_DECODE_2PASS, sp.PATH_PREFILL]
+ALL_PATHS_SMALL = [sp.PATH_DECODE, sp.PATH_DECODE_2PASS, sp.PATH_PREFILL, sp.PATH_PREFILL_LARGE]
 
 
 def test_library_is_in_tree():
@@ -81,8 +81,10 @@ def test_gate_parity(M, K, hard, tau):
 # ----------------------------------------------------------- one-hot probe
 
 @pytest.mark.parametrize("path,M", [(sp.PATH_DECODE, 16), (sp.PATH_DECODE, 3),
+                                    (sp.PATH_DECODE, 1),
                                     (sp.PATH_DECODE_2PASS, 16), (sp.PATH_PREFILL, 16),
-                                    (sp.PATH_PREFILL, 40), (sp.PATH_PREFILL, 200)])
+                                    (sp.PATH_PREFILL, 40), (sp.PATH_PREFILL, 200),
+                                    (sp.PATH_PREFILL_LARGE, 16), (sp.PATH_PREFILL_LARGE, 200)])
 @pytest.mark.parametrize("K", [256, 4096])
 def test_one_hot_unpack_probe(path, M, K):
     """x[m] = e_{k_m}, s = 1: y[m][n] = u[n][k_m] - z_n exactly (fp32 output).  Pins
@@ -190,7 +192,7 @@ def random_case(M, N, K, r, kind, hard, seed):
 
 RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 256),
           (17, 1000, 160, 40), (33, 24, 4096, 8), (100, 200, 544, 64), (130, 129, 1024, 32),
-          (257, 300, 2080, 24)]
+          (257, 300, 2080, 24), (200, 300, 352, 32), (129, 513, 192, 16)]
 
 
 @pytest.mark.parametrize("M,N,K,r", RAGGED)
@@ -200,7 +202,7 @@ def test_ragged_shapes(M, N, K, r, kind, hard):
     d = random_case(M, N, K, r, kind, hard, seed=M * 1000 + N + K + r + kind * 7 + hard)
     ref = run_oracle(d)
     gref = oracle.gate(d["x"], d["ec"]["w_g"], d["ec"]["b"], d["ec"]["tau"], hard)
-    paths = ALL_PATHS_SMALL if M <= 16 else [sp.PATH_PREFILL]
+    paths = ALL_PATHS_SMALL if M <= 16 else [sp.PATH_PREFILL, sp.PATH_PREFILL_LARGE]
     for path in paths:
         y, e = run_gpu(d, path=path)
         assert_close(y, ref, f"ragged {M}x{N}x{K} r={r} kind={kind} hard={hard} path={path}")

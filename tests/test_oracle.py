@@ -55,7 +55,7 @@ def test_pack_worked_example():
     assert bad == 0 and p.tolist() == [g["u4"]["bytes"]]
     # little-endian 32-bit view of the signed example
     p, _ = oracle.pack_w4(np.array([g["s4"]["codes"]], dtype=np.int8), oracle.CODES_S4)
-    assert int(p.view("<u4")[0, 0]) == 0x3D5BF870
+    assert int(p.view("<u4")[0, 0]) == int(g["s4"]["word_le"], 16)
 
 
 @pytest.mark.parametrize("kind", [oracle.CODES_S4, oracle.CODES_U4])
@@ -74,19 +74,25 @@ def test_pack_roundtrip_exhaustive(kind):
     p, bad = oracle.pack_w4(codes, kind)
     assert bad == 0
     assert np.array_equal(oracle.unpack_w4(p, K), u)
-    # the byte holding position pos carries v in the nibble the layout names
+    # code k of a row sits in word k // 8 at nibble position i // 2 (even i)
+    # or 4 + i // 2 (odd i), i = k % 8; every other nibble of the row is 0
     for i, (pos, v) in enumerate((pos, v) for pos in range(K) for v in range(16)):
-        byte = int(p[i, pos // 2])
-        other = 0
-        want = (v | (other << 4)) if pos % 2 == 0 else (other | (v << 4))
-        assert byte == want
+        word = int(p[i].view("<u4")[pos // 8])
+        j = pos % 8
+        nib = j // 2 if j % 2 == 0 else 4 + j // 2
+        assert word == v << (4 * nib)
+        assert np.count_nonzero(p[i]) == (1 if v else 0)
 
 
 def test_unpack_all_bytes():
+    # byte b of word w: low nibble = code 8w + perm[2b], high = code 8w + perm[2b+1]
+    perm = (0, 2, 4, 6, 1, 3, 5, 7)
     p = np.arange(256, dtype=np.uint8).reshape(1, 256)
     u = oracle.unpack_w4(p, 512)[0]
-    assert np.array_equal(u[0::2], np.arange(256) & 15)
-    assert np.array_equal(u[1::2], np.arange(256) >> 4)
+    for B in range(256):
+        w, b = divmod(B, 4)
+        assert u[8 * w + perm[2 * b]] == B & 15
+        assert u[8 * w + perm[2 * b + 1]] == B >> 4
 
 
 def test_pack_bad_codes_counted_and_masked():
@@ -94,10 +100,10 @@ def test_pack_bad_codes_counted_and_masked():
     p, bad = oracle.pack_w4(c, oracle.CODES_S4)
     assert bad == 4
     assert oracle.unpack_w4(p, 8).tolist() == [[(v + 8) & 15 for v in c[0].tolist()]]
-    c = np.array([[16, 15, 255, 0]], dtype=np.uint8)
+    c = np.array([[16, 15, 255, 0, 1, 2, 3, 4]], dtype=np.uint8)
     p, bad = oracle.pack_w4(c, oracle.CODES_U4)
     assert bad == 2
-    assert oracle.unpack_w4(p, 4).tolist() == [[0, 15, 15, 0]]
+    assert oracle.unpack_w4(p, 8).tolist() == [[0, 15, 15, 0, 1, 2, 3, 4]]
 
 
 def test_dequant_closed_form():
