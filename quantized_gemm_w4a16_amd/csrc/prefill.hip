@@ -17,7 +17,8 @@ namespace {
 // One workgroup per 16 tokens; its PRE_WAVES waves split K.  Per token: gate logit in
 // fp64, g, hard-gate flag, u = A x (fp32 via MFMA, natural depth order on both
 // operands), v = g u (0 for skipped tokens) stored as bf16 hi + lo.
-constexpr int PRE_WAVES = 16;
+constexpr int PRE_WAVES = 8;
+constexpr int PRE_T = 8;          // 32-deep steps whose loads are in flight together
 
 __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArgs a)
 {
@@ -30,7 +31,11 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, K = a.K;
     const int64_t m0 = (int64_t)blockIdx.x * 16;
-    const int64_t T = K / 32, t0 = wave * T / PRE_WAVES, t1 = (wave + 1) * T / PRE_WAVES;
+    // Wave w takes K slice (w + block) % PRE_WAVES: workgroups running side by
+    // side then read different parts of A (which every workgroup reads whole)
+    // instead of all hitting the same L2 lines at once.
+    const int64_t T = K / 32, slice = (wave + blockIdx.x) % PRE_WAVES;
+    const int64_t t0 = slice * T / PRE_WAVES, t1 = (slice + 1) * T / PRE_WAVES;
     const int64_t m = m0 + lr;
     const bool mv = m < M;
     const int rpad = a.rpad, r = a.r;
@@ -42,20 +47,33 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
         f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
         double zp = 0.0;
         const int j0 = 32 * jp + lr, j1 = j0 + 16;
-        for (int64_t t = t0; t < t1; t++) {
-            const int64_t k = 32 * t + 8 * lg;
-            const u32x4 xf = mv ? ld16(a.x + m * K + k) : zero4();
-            const u32x4 a0 = (j0 < r) ? ld16(a.A + (int64_t)j0 * K + k) : zero4();
-            const u32x4 a1 = (j1 < r) ? ld16(a.A + (int64_t)j1 * K + k) : zero4();
-            u0 = mfma16(a0, xf, u0);
-            u1 = mfma16(a1, xf, u1);
-            if (jp == 0) {
-                const u32x4 wv = ld16(a.wg + k);
+        // PRE_T 32-deep steps at a time: every load of a chunk is issued before
+        // any is used, so one memory round trip covers the chunk.
+        for (int64_t tc = t0; tc < t1; tc += PRE_T) {
+            u32x4 xf[PRE_T], a0[PRE_T], a1[PRE_T], wv[PRE_T];
 #pragma unroll
-                for (int e = 0; e < 4; e++) {
-                    zp += (double)(__uint_as_float(xf[e] << 16) * __uint_as_float(wv[e] << 16));
-                    zp += (double)(__uint_as_float(xf[e] & 0xFFFF0000u) *
-                                   __uint_as_float(wv[e] & 0xFFFF0000u));
+            for (int i = 0; i < PRE_T; i++) {
+                const int64_t t = tc + i < t1 ? tc + i : t1 - 1;   // clamped; dropped below
+                const int64_t k = 32 * t + 8 * lg;
+                xf[i] = mv ? ld16(a.x + m * K + k) : zero4();
+                a0[i] = (j0 < r) ? ld16(a.A + (int64_t)j0 * K + k) : zero4();
+                a1[i] = (j1 < r) ? ld16(a.A + (int64_t)j1 * K + k) : zero4();
+                wv[i] = (jp == 0) ? ld16(a.wg + k) : zero4();
+            }
+#pragma unroll
+            for (int i = 0; i < PRE_T; i++) {
+                if (tc + i < t1) {
+                    u0 = mfma16(a0[i], xf[i], u0);
+                    u1 = mfma16(a1[i], xf[i], u1);
+                    if (jp == 0) {
+#pragma unroll
+                        for (int e = 0; e < 4; e++) {
+                            zp += (double)(__uint_as_float(xf[i][e] << 16) *
+                                           __uint_as_float(wv[i][e] << 16));
+                            zp += (double)(__uint_as_float(xf[i][e] & 0xFFFF0000u) *
+                                           __uint_as_float(wv[i][e] & 0xFFFF0000u));
+                        }
+                    }
                 }
             }
         }
