@@ -15,7 +15,10 @@ The line also carries the plain-W4 time of the same steps (EC overhead), the
 roofline of the decode kernel and the CPU oracle timed on a bounded sample.
 
 --workload c4 times the prefill configuration instead (M = N = K = 4096,
-TFLOP/s); it is not the default line.
+TFLOP/s); --workload c3 the MLP up-projection at M = 64 (K = 4096, N = 14336,
+rank 64, hard gate); --workload c5 a 28-layer stack of a 1.5B-class decoder's
+seven linears (ECs on 4 layers) at --c5-m tokens, reporting the stack time
+and the EC share.  None of these is the default line.
 """
 from __future__ import annotations
 
@@ -41,7 +44,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="c2", choices=["c2", "c4"])
+    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--c5-m", type=int, default=1, choices=[1, 16, 128, 2048],
+                   help="tokens per call of the C5 stack")
     p.add_argument("--copies", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -265,6 +270,117 @@ def run_c4(args, torch, sp, gen):
     }
 
 
+def run_c3(args, torch, sp, gen):
+    """C3: M = 64, K = 4096, N = 14336, EC rank 64 with the hard gate (about 40 %
+    of tokens skip).  Near the ridge: GB/s and TFLOP/s both reported."""
+    d = gen.make(3)
+    M, N, K, r = d["M"], d["N"], d["K"], d["ec"]["r"]
+    R = max(2, min(args.copies, 16))                     # 16 x 29 MB > 2 x the Infinity Cache
+    ws, ecs = build_copies(d, R, torch, sp)
+    x = dev(d["x"], torch)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    wsp = sp.new_workspace(M, N, K, r)
+
+    def steps_fn(use_ec):
+        def record(n):
+            for i in range(n):
+                sp.spear_w4_linear(x, ws[i % R], ecs[i % R] if use_ec else None, y=y,
+                                   workspace=wsp)
+        return record
+
+    for _ in range(args.warmup):
+        steps_fn(True)(1)
+    torch.cuda.synchronize()
+    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
+    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    w, ecb, io = layer_bytes(M, N, K, r, True)
+    ms = t_ec / args.steps
+    gbs = (w + ecb + io) / (ms * 1e-3) / 1e9
+    flops = 2.0 * M * N * K + 2.0 * M * K * r + 2.0 * M * r * N
+    return {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "C3 MLP up-projection: M=64, K=4096, N=14336, int4 asymmetric "
+                               "per-channel, x N(0,1) with 1% of channels x20, EC rank 64, "
+                               "hard gate (~40% of tokens skip), fp32 output",
+                   "rotating_weight_copies": R},
+        "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+        "ec_overhead": round(t_ec / t_plain - 1.0, 4),
+        "plain_GBps": round((w + io) / (t_plain / args.steps * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "prepass_kernel + gemm_kernel<2,2,2,2,1,1>"},
+    }
+
+
+def run_c5(args, torch, sp, gen):
+    """C5: the stack of 28 layers x 7 linears (q, k, v, o 2048 -> 2048; gate, up
+    2048 -> 8192; down 8192 -> 2048) with ECs on 4 seeded layers, one call per
+    linear at M tokens, each layer with its own weights (896 MB packed, so the
+    stack streams from HBM).  One step = the whole stack; EC share = the stack
+    time the ECs add, over the compensated stack time."""
+    M = args.c5_m
+    layers = []
+    ec_layers = set(gen.c5_ec_layers())
+    for layer in range(gen.C5_LAYERS):
+        for lin in gen.C5_LINEARS:
+            d = gen.make_c5(layer, lin, M)
+            codes = dev(d["codes"], torch)
+            w = sp.W4(sp.spear_pack_w4(codes, d["kind"]), dev(d["scales"], torch),
+                      dev(d["zeros"], torch), d["N"], d["K"])
+            del codes
+            e = d["ec"]
+            ec = (sp.EC(dev(e["A"], torch), dev(e["B"], torch), dev(e["w_g"], torch), e["b"],
+                        e["tau"], e["hard"]) if e is not None else None)
+            layers.append((d["N"], d["K"], w, ec, e["r"] if e is not None else 0))
+    xs = {K: dev(gen.make_c5(0, "down" if K == gen.C5_FF else "q", M)["x"], torch)
+          for K in (gen.C5_D, gen.C5_FF)}
+    ys = {N: torch.empty((M, N), dtype=torch.float32, device="cuda") for N in (gen.C5_D, gen.C5_FF)}
+    wsp = sp.new_workspace(M, gen.C5_FF, gen.C5_FF, 32)
+
+    def steps_fn(use_ec):
+        def record(n):
+            for _ in range(n):
+                for (N, K, w, ec, r) in layers:
+                    sp.spear_w4_linear(xs[K], w, ec if use_ec else None, y=ys[N], workspace=wsp)
+        return record
+
+    for _ in range(args.warmup):
+        steps_fn(True)(1)
+    torch.cuda.synchronize()
+    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
+    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    assert sp.spear_workspace_timeouts(wsp) == 0
+    byts = sum(sum(layer_bytes(M, N, K, r, True)) for (N, K, w, ec, r) in layers)
+    flops = sum(2.0 * M * N * K + (2.0 * M * K * r + 2.0 * M * r * N if r else 0.0)
+                for (N, K, w, ec, r) in layers)
+    ms = t_ec / args.steps
+    big = M >= 128
+    val = flops / (ms * 1e-3) / 1e12 if big else byts / (ms * 1e-3) / 1e9
+    unit = "TFLOP/s" if big else "GB/s"
+    peak = BF16_PEAK_TFLOPS if big else HBM_PEAK_GBS
+    return {
+        "metric": METRIC, "value": round(val, 2), "unit": unit, "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"C5 decoder stack: 28 layers x (q,k,v,o 2048->2048, gate,up "
+                               f"2048->8192, down 8192->2048), M={M}, int4 asymmetric "
+                               f"per-channel, ECs rank 32 hard gate on layers "
+                               f"{sorted(ec_layers)}, fp32 output",
+                   "linears_per_step": len(layers)},
+        "stack_ms": round(ms, 4),
+        "plain_stack_ms": round(t_plain / args.steps, 4),
+        "ec_share": round((t_ec - t_plain) / t_ec, 4),
+        "ec_overhead": round(t_ec / t_plain - 1.0, 4),
+        "roofline": {"bound": "mfma" if big else "hbm", "achieved": round(val, 2), "peak": peak,
+                     "unit": unit, "frac": round(val / peak, 4), "traffic": None,
+                     "kernel": "whole stack (all kernels)"},
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -278,7 +394,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     sp.load()
-    out = run_c2(args, torch, sp, gen) if args.workload == "c2" else run_c4(args, torch, sp, gen)
+    run = {"c2": run_c2, "c3": run_c3, "c4": run_c4, "c5": run_c5}[args.workload]
+    out = run(args, torch, sp, gen)
     if args.copy_calibration:
         out["copy_calibration_bytes"] = copy_calibration(torch)
     if args.workload == "c2" and not args.no_cpu_baseline:
