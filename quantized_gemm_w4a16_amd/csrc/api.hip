@@ -77,7 +77,7 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
         L.pz = off;
         off = align256(off + (size_t)(nprod_max * 16 * 2) * sizeof(uint64_t));
     }
-    L.vhi = L.vlo = L.active = off;
+    L.vhi = L.vlo = L.active = L.preu = L.prez = off;
     if (r > 0) {
         L.vhi = off;
         off = align256(off + (size_t)(L.mpad * L.rpad) * 2);
@@ -85,6 +85,12 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
         off = align256(off + (size_t)(L.mpad * L.rpad) * 2);
         L.active = off;
         off = align256(off + (size_t)L.mpad * 4);
+        // EC pre-pass with K split over workgroups: per-slot partials (sized
+        // independently of M).
+        L.preu = off;
+        off = align256(off + (size_t)PRE_SLOTS * 16 * L.rpad * sizeof(float));
+        L.prez = off;
+        off = align256(off + (size_t)PRE_SLOTS * 16 * sizeof(double));
     }
     L.total = off;
     return L;
@@ -303,6 +309,18 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
     a.nprod = L.nprod;
     a.prod_k = L.prod_k;
     a.mpad = L.mpad;
+    {
+        // EC pre-pass: few token groups split K so that about 256 workgroups
+        // run, each over at least 8 steps of 32.
+        const int64_t tg = cdiv(M > 0 ? M : 1, 16), T = K / 32;
+        int64_t ks = 1;
+        if (tg < PRE_GROUPS) {
+            ks = cdiv(256, tg);
+            const int64_t most = T / 8 > 0 ? T / 8 : 1;
+            ks = ks < most ? ks : most;
+        }
+        a.pre_ks = ks;
+    }
     a.L = L;
     a.out_f32 = out_dtype == SPEAR_OUT_F32;
     a.wait_limit = g_wait_limit ? g_wait_limit : DEFAULT_WAIT_LIMIT;

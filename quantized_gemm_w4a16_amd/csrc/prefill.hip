@@ -14,113 +14,223 @@ namespace spear {
 namespace {
 
 // --------------------------------------------------------------------- pre-pass
-// One workgroup per 16 tokens; its PRE_WAVES waves split K.  Per token: gate logit in
-// fp64, g, hard-gate flag, u = A x (fp32 via MFMA, natural depth order on both
-// operands), v = g u (0 for skipped tokens) stored as bf16 hi + lo.
+// Per token: gate logit in fp64, g, hard-gate flag, u = A x (fp32 via MFMA,
+// natural depth order on both operands), v = g u (0 for skipped tokens) stored
+// as bf16 hi + lo.  Workgroup (group, slice): 16 tokens over one of pre_ks K
+// slices; its PRE_WAVES waves split the slice (wave w takes part
+// (w + block) % PRE_WAVES, so workgroups side by side read different parts of
+// A).  A wave walks its part in chunks of PRE_T 32-deep steps and, per chunk,
+// issues every load (x, up to PRE_RT 16-rank tiles of A, w_g) before it uses
+// any, so one memory round trip covers the chunk.  With one slice the
+// workgroup finishes the tokens itself; with several it stores its partials in
+// the workspace and a second launch (prepass_combine) sums the slices of each
+// group in order and finishes them.  (A release fence and counter inside one
+// launch would instead write back the whole L2 once per workgroup.)
 constexpr int PRE_WAVES = 8;
-constexpr int PRE_T = 8;          // 32-deep steps whose loads are in flight together
+constexpr int PRE_T = 8;                       // 32-deep steps per chunk
+constexpr int PRE_RT = 4;                      // 16-rank tiles per pass over the slice
+constexpr int PRE_TILES = SPEAR_MAX_RANK / 16;
+constexpr int CMB_WAVES = 4;                   // combine: waves over the u tiles (one more sums z)
+constexpr int CMB_U = 16;                      // slot loads a combine thread has in flight
+
+// The last step of the pre-pass for tokens m0 .. m0 + 15, given their logit
+// sums (without b) in s_zw and u in s_uw (tile t, lane l: ranks 16 t + 4 (l / 16)
+// + i of token l % 16): gate, selection, v = g u as bf16 hi + lo.  Called by
+// every thread of the workgroup; waves below nwaves write v.
+__device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_uw)[64],
+                               const double *s_zw, float *s_g, int *s_act, int tid, int lane,
+                               int wave, int nwaves)
+{
+    const int lr = lane & 15, lg = lane >> 4;
+    const int64_t M = a.M, m = m0 + lr;
+    const int rpad = a.rpad;
+    uint16_t *vhi = reinterpret_cast<uint16_t *>(a.ws + a.L.vhi);
+    uint16_t *vlo = reinterpret_cast<uint16_t *>(a.ws + a.L.vlo);
+    int32_t *active = reinterpret_cast<int32_t *>(a.ws + a.L.active);
+    if (tid < 16) {
+        const double z = (double)a.b + s_zw[tid];
+        const int64_t mm = m0 + tid;
+        const float g = (float)(1.0 / (1.0 + exp(-z)));
+        const int act = (mm < M) && (a.hard ? (z > a.thr) : 1);
+        s_g[tid] = g;
+        s_act[tid] = act;
+        active[mm] = act;
+        if (mm < M && a.g_out)
+            a.g_out[mm] = g;
+    }
+    __syncthreads();
+    // rows m >= M (up to the 16-row padding) get v = 0
+    const float g = s_act[lr] ? s_g[lr] : 0.f;
+    for (int tile = wave; wave < nwaves && tile < rpad / 16; tile += nwaves) {
+        const f32x4 u = s_uw[tile][lane];
+        uint16_t hi[4], lo[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const float v = g * u[i];
+            hi[i] = f2bf(v);
+            lo[i] = f2bf(v - bf16f(hi[i]));
+        }
+        const int64_t off = m * rpad + 16 * tile + 4 * lg;
+        uint2 h, l;
+        h.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+        h.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+        l.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+        l.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+        *reinterpret_cast<uint2 *>(vhi + off) = h;
+        *reinterpret_cast<uint2 *>(vlo + off) = l;
+    }
+}
 
 __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArgs a)
 {
-    __shared__ f32x4 s_u[PRE_WAVES][2][64];
+    __shared__ f32x4 s_u[PRE_WAVES][PRE_RT][64];
     __shared__ double s_z[PRE_WAVES][64];
+    __shared__ u32x4 s_wg[PRE_WAVES][4 * PRE_T];   // each wave's w_g for its chunk
+    __shared__ f32x4 s_uw[PRE_TILES][64];          // the workgroup's u
+    __shared__ double s_zw[16];
     __shared__ float s_g[16];
     __shared__ int s_act[16];
     pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int64_t M = a.M, K = a.K;
-    const int64_t m0 = (int64_t)blockIdx.x * 16;
-    // Wave w takes K slice (w + block) % PRE_WAVES: workgroups running side by
-    // side then read different parts of A (which every workgroup reads whole)
-    // instead of all hitting the same L2 lines at once.
-    const int64_t T = K / 32, slice = (wave + blockIdx.x) % PRE_WAVES;
-    const int64_t t0 = slice * T / PRE_WAVES, t1 = (slice + 1) * T / PRE_WAVES;
+    const int64_t M = a.M, K = a.K, KS = a.pre_ks;
+    const int64_t grp = blockIdx.x / KS, ks = blockIdx.x % KS;
+    const int64_t m0 = grp * 16;
+    const int64_t T = K / 32, s0 = ks * T / KS, s1 = (ks + 1) * T / KS;
+    const int64_t part = (wave + blockIdx.x) % PRE_WAVES;
+    const int64_t t0 = s0 + part * (s1 - s0) / PRE_WAVES, t1 = s0 + (part + 1) * (s1 - s0) / PRE_WAVES;
     const int64_t m = m0 + lr;
     const bool mv = m < M;
-    const int rpad = a.rpad, r = a.r;
-    uint16_t *vhi = reinterpret_cast<uint16_t *>(a.ws + a.L.vhi);
-    uint16_t *vlo = reinterpret_cast<uint16_t *>(a.ws + a.L.vlo);
-    int32_t *active = reinterpret_cast<int32_t *>(a.ws + a.L.active);
+    const int r = a.r, ntile = a.rpad / 16;
 
-    for (int jp = 0; jp < rpad / 32; jp++) {
-        f32x4 u0 = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < ntile; q0 += PRE_RT) {
+        f32x4 acc[PRE_RT];
+#pragma unroll
+        for (int q = 0; q < PRE_RT; q++)
+            acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
         double zp = 0.0;
-        const int j0 = 32 * jp + lr, j1 = j0 + 16;
-        // PRE_T 32-deep steps at a time: every load of a chunk is issued before
-        // any is used, so one memory round trip covers the chunk.
         for (int64_t tc = t0; tc < t1; tc += PRE_T) {
-            u32x4 xf[PRE_T], a0[PRE_T], a1[PRE_T], wv[PRE_T];
+            const int n = (int)(t1 - tc < PRE_T ? t1 - tc : PRE_T);   // wave-uniform
+            u32x4 xf[PRE_T], av[PRE_T][PRE_RT];
 #pragma unroll
             for (int i = 0; i < PRE_T; i++) {
-                const int64_t t = tc + i < t1 ? tc + i : t1 - 1;   // clamped; dropped below
-                const int64_t k = 32 * t + 8 * lg;
-                xf[i] = mv ? ld16(a.x + m * K + k) : zero4();
-                a0[i] = (j0 < r) ? ld16(a.A + (int64_t)j0 * K + k) : zero4();
-                a1[i] = (j1 < r) ? ld16(a.A + (int64_t)j1 * K + k) : zero4();
-                wv[i] = (jp == 0) ? ld16(a.wg + k) : zero4();
+                const int64_t k = 32 * (tc + i) + 8 * lg;
+                xf[i] = (i < n && mv) ? ld16(a.x + m * K + k) : zero4();
+#pragma unroll
+                for (int q = 0; q < PRE_RT; q++) {
+                    const int j = 16 * (q0 + q) + lr;
+                    av[i][q] = (i < n && j < r) ? ld16(a.A + (int64_t)j * K + k) : zero4();
+                }
             }
+            // lane 4 i + p holds w_g[32 (tc + i) + 8 p .. + 7]
+            const u32x4 wq = (q0 == 0 && lane < 4 * n) ? ld16(a.wg + 32 * tc + 8 * lane) : zero4();
+            if (q0 == 0 && lane < 4 * PRE_T)
+                s_wg[wave][lane] = wq;
 #pragma unroll
             for (int i = 0; i < PRE_T; i++) {
-                if (tc + i < t1) {
-                    u0 = mfma16(a0[i], xf[i], u0);
-                    u1 = mfma16(a1[i], xf[i], u1);
-                    if (jp == 0) {
+                if (i < n) {
+#pragma unroll
+                    for (int q = 0; q < PRE_RT; q++)
+                        if (q0 + q < ntile)
+                            acc[q] = mfma16(av[i][q], xf[i], acc[q]);
+                    if (q0 == 0) {
+                        const u32x4 w = s_wg[wave][4 * i + lg];
 #pragma unroll
                         for (int e = 0; e < 4; e++) {
                             zp += (double)(__uint_as_float(xf[i][e] << 16) *
-                                           __uint_as_float(wv[i][e] << 16));
+                                           __uint_as_float(w[e] << 16));
                             zp += (double)(__uint_as_float(xf[i][e] & 0xFFFF0000u) *
-                                           __uint_as_float(wv[i][e] & 0xFFFF0000u));
+                                           __uint_as_float(w[e] & 0xFFFF0000u));
                         }
                     }
                 }
             }
         }
-        s_u[wave][0][lane] = u0;
-        s_u[wave][1][lane] = u1;
-        if (jp == 0)
+#pragma unroll
+        for (int q = 0; q < PRE_RT; q++)
+            s_u[wave][q][lane] = acc[q];
+        if (q0 == 0)
             s_z[wave][lane] = zp;
         __syncthreads();
-        if (jp == 0 && tid < 16) {
-            double z = (double)a.b;
-            for (int w = 0; w < PRE_WAVES; w++)
-                for (int q = 0; q < 4; q++)
-                    z += s_z[w][tid + 16 * q];
-            const int64_t mm = m0 + tid;
-            const float g = (float)(1.0 / (1.0 + exp(-z)));
-            const int act = (mm < M) && (a.hard ? (z > a.thr) : 1);
-            s_g[tid] = g;
-            s_act[tid] = act;
-            active[mm] = act;
-            if (mm < M && a.g_out)
-                a.g_out[mm] = g;
-        }
-        __syncthreads();
-        if (wave < 2) {
+        // the workgroup's partials: waves in order (then lane groups for z)
+        if (wave < PRE_RT && q0 + wave < ntile) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
             for (int w = 0; w < PRE_WAVES; w++)
                 u += s_u[w][wave][lane];
-            // lane holds u[rank 32 jp + 16 wave + 4 lg + i][token m0 + lr]
-            const float g = s_act[lr] ? s_g[lr] : 0.f;
-            uint16_t hi[4], lo[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const float v = g * u[i];
-                hi[i] = f2bf(v);
-                lo[i] = f2bf(v - bf16f(hi[i]));
-            }
-            const int64_t off = m * rpad + 32 * jp + 16 * wave + 4 * lg;
-            uint2 h, l;
-            h.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
-            h.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
-            l.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-            l.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
-            *reinterpret_cast<uint2 *>(vhi + off) = h;
-            *reinterpret_cast<uint2 *>(vlo + off) = l;
+            s_uw[q0 + wave][lane] = u;
+        }
+        if (q0 == 0 && wave == PRE_RT && lane < 16) {
+            double z = 0.0;
+            for (int w = 0; w < PRE_WAVES; w++)
+                for (int q = 0; q < 4; q++)
+                    z += s_z[w][lane + 16 * q];
+            s_zw[lane] = z;
         }
         __syncthreads();
     }
+
+    if (KS > 1) {
+        // Partials to this workgroup's slot (16 rpad floats and 16 doubles);
+        // prepass_combine finishes the group.
+        f32x4 *pu = reinterpret_cast<f32x4 *>(a.ws + a.L.preu);
+        double *pz = reinterpret_cast<double *>(a.ws + a.L.prez);
+        const int64_t slot = grp * KS + ks;
+        for (int tile = wave; tile < ntile; tile += PRE_WAVES)
+            pu[(slot * ntile + tile) * 64 + lane] = s_uw[tile][lane];
+        if (tid < 16)
+            pz[slot * 16 + tid] = s_zw[tid];
+        return;
+    }
+    prepass_finish(a, m0, s_uw, s_zw, s_g, s_act, tid, lane, wave, PRE_WAVES);
+}
+
+// Second launch of a split pre-pass: workgroup g sums the pre_ks slots of token
+// group g in slice order and finishes its 16 tokens.  Waves 0 .. CMB_WAVES - 1
+// sum the u tiles, wave CMB_WAVES the logits.
+__global__ __launch_bounds__(64 * (CMB_WAVES + 1)) void prepass_combine(const LinearArgs a)
+{
+    __shared__ f32x4 s_uw[PRE_TILES][64];
+    __shared__ double s_zw[16];
+    __shared__ float s_g[16];
+    __shared__ int s_act[16];
+    pin_args(a);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t KS = a.pre_ks, grp = blockIdx.x;
+    const int ntile = a.rpad / 16;
+    const f32x4 *pu = reinterpret_cast<const f32x4 *>(a.ws + a.L.preu);
+    const double *pz = reinterpret_cast<const double *>(a.ws + a.L.prez);
+    for (int tile = wave; wave < CMB_WAVES && tile < ntile; tile += CMB_WAVES) {
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
+            f32x4 v[CMB_U];
+#pragma unroll
+            for (int i = 0; i < CMB_U; i++)
+                if (q0 + i < KS)
+                    v[i] = pu[((grp * KS + q0 + i) * ntile + tile) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < CMB_U; i++)
+                if (q0 + i < KS)
+                    u += v[i];
+        }
+        s_uw[tile][lane] = u;
+    }
+    if (wave == CMB_WAVES && lane < 16) {
+        double z = 0.0;
+        for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
+            double v[CMB_U];
+#pragma unroll
+            for (int i = 0; i < CMB_U; i++)
+                if (q0 + i < KS)
+                    v[i] = pz[(grp * KS + q0 + i) * 16 + lane];
+#pragma unroll
+            for (int i = 0; i < CMB_U; i++)
+                if (q0 + i < KS)
+                    z += v[i];
+        }
+        s_zw[lane] = z;
+    }
+    __syncthreads();
+    prepass_finish(a, grp * 16, s_uw, s_zw, s_g, s_act, tid, lane, wave, CMB_WAVES);
 }
 
 // ------------------------------------------------------------------------ GEMM
@@ -654,8 +764,15 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
 
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(prepass_kernel, dim3((unsigned)((a.M + 15) / 16)), dim3(64 * PRE_WAVES), 0,
+    const unsigned groups = (unsigned)((a.M + 15) / 16);
+    hipLaunchKernelGGL(prepass_kernel, dim3(groups * (unsigned)a.pre_ks), dim3(64 * PRE_WAVES), 0,
                        s, a);
+    if (a.pre_ks > 1) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(prepass_combine, dim3(groups), dim3(64 * (CMB_WAVES + 1)), 0, s, a);
+    }
     return hipGetLastError();
 }
 

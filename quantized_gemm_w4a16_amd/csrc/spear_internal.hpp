@@ -147,9 +147,12 @@ constexpr int EPOCH_STRIDE = 128;
 constexpr int PROD_BYTES = 16384; // bytes of A an EC producer workgroup reads, about
 constexpr int MAX_PROD = 32;      // at most this many EC producer workgroups
 constexpr int PROD_CHUNK = 4;     // producer partials a consumer wave loads per batch
+constexpr int PRE_SLOTS = 512;    // EC pre-pass: (token group, K slice) partial slots, at most
+                                  // (fewer than PRE_GROUPS groups, about 256 workgroups)
+constexpr int PRE_GROUPS = 128;   // EC pre-pass: token groups below which K is split
 
 struct WsLayout {
-    size_t hdr, epoch, zeros, colcnt, splitp, pu, pz, vhi, vlo, active, total;
+    size_t hdr, epoch, zeros, colcnt, splitp, pu, pz, vhi, vlo, active, preu, prez, total;
     int64_t ncg, ksplit, spw, nprod, prod_k, rpad, mpad;
 };
 
@@ -173,6 +176,7 @@ struct LinearArgs {
     int32_t r, rpad;
     int64_t M, N, K;
     int64_t ncg, ksplit, spw, nprod, prod_k, mpad;
+    int64_t pre_ks;  // EC pre-pass: K slices per token group
     WsLayout L;
     uint32_t wait_limit;
     int32_t out_f32;
@@ -210,6 +214,7 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.idx_out); pin_arg(a.nact_out); pin_arg(a.thr); pin_arg(a.b); pin_arg(a.hard);
     pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
     pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
+    pin_arg(a.pre_ks); pin_arg(a.L.preu); pin_arg(a.L.prez);
     pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.colcnt); pin_arg(a.L.splitp); pin_arg(a.L.pu);
     pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);
