@@ -32,6 +32,46 @@ static int64_t ec_producers(int64_t mr, int64_t K, int64_t rpad, int64_t *prod_k
     return cdiv(K, DEC_WAVES * *prod_k);
 }
 
+// MFMA GEMM tiling: tokens per tile, and the K slices a tile is split into so
+// that about 256 workgroups run, each over at least 4 stages of 128 (one slice
+// when the path takes whole tiles).
+static int64_t gemm_bm(int64_t M, int whole) { return (!whole && M <= 64) ? 64 : 128; }
+
+static int64_t gemm_ks(int64_t M, int64_t N, int64_t K, int whole)
+{
+    if (whole)
+        return 1;
+    const int64_t bm = gemm_bm(M, 0);
+    const int64_t tiles = cdiv(N, 256) * cdiv(M > 0 ? M : 1, bm);
+    const int64_t most = cdiv(K, 128) / 4;
+    int64_t ks = 256 / tiles;
+    ks = ks < most ? ks : most;
+    return ks > 1 ? ks : 1;
+}
+
+// Bytes of fp32 partial tiles a split GEMM writes for M tokens: one
+// bm x 256 tile per (slice, tile).  The region is sized for the most any token
+// count up to M needs, so that a workspace sized for M serves every smaller M.
+static size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K)
+{
+    auto need = [&](int64_t m) -> size_t {
+        const int64_t ks = gemm_ks(m, N, K, 0), bm = gemm_bm(m, 0);
+        return ks > 1 ? (size_t)(ks * cdiv(N, 256) * cdiv(m, bm) * bm * 256) * sizeof(float) : 0;
+    };
+    const int64_t m1 = M < 1 ? 1 : M;
+    size_t best = need(m1 < 64 ? m1 : 64);            // up to 64 tokens: one 64-token tile row
+    if (m1 > 64) {
+        for (int64_t tm = 1;; tm++) {                 // tm rows of 128-token tiles
+            const int64_t m = 128 * tm < m1 ? 128 * tm : m1;
+            const size_t b = need(m);
+            best = b > best ? b : best;
+            if (128 * tm >= m1 || gemm_ks(m, N, K, 0) == 1)
+                break;                                // no split for more rows either
+        }
+    }
+    return best;
+}
+
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
 {
     WsLayout L;
@@ -92,6 +132,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
         L.prez = off;
         off = align256(off + (size_t)PRE_SLOTS * 16 * sizeof(double));
     }
+    L.gpart = off;
+    off = align256(off + gemm_part_bytes(M, N, K));
     L.total = off;
     return L;
 }
@@ -321,6 +363,8 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
         }
         a.pre_ks = ks;
     }
+    a.g_bm = gemm_bm(M, path == SPEAR_PATH_PREFILL_LARGE);
+    a.g_ks = gemm_ks(M, N, K, path == SPEAR_PATH_PREFILL_LARGE);
     a.L = L;
     a.out_f32 = out_dtype == SPEAR_OUT_F32;
     a.wait_limit = g_wait_limit ? g_wait_limit : DEFAULT_WAIT_LIMIT;

@@ -234,251 +234,9 @@ __global__ __launch_bounds__(64 * (CMB_WAVES + 1)) void prepass_combine(const Li
 }
 
 // ------------------------------------------------------------------------ GEMM
-// Output tile BN channels x BM tokens, computed as W x^T so each lane ends with
-// 4 consecutive channels of one token (contiguous stores).  K advances in
-// 128-deep super-steps.  Packed weights: HBM -> registers (16-byte loads, one
-// super-step of prefetch), unpacked to bf16 (1 + u/16) pairs in registers.
-// Activations: HBM -> registers -> LDS (double-buffered), summed per token on
-// the way for the epilogue's offset removal.  Epilogue: y = s_n (16 acc - (16 + z_n) sum_k x) + B v.
-template <int FN, int FM, int WNW, int WMW, int EC, int OUT_F32>
-__global__ __launch_bounds__(64 * WNW * WMW) void gemm_kernel(const LinearArgs a)
-{
-    constexpr int NT = 64 * WNW * WMW;
-    constexpr int BN = 16 * FN * WNW, BM = 16 * FM * WMW;
-    constexpr int RS = 272;               // LDS bytes per token row: 16 chunks + pad
-    constexpr int CPT = BM * 16 / NT;     // 16-byte activation chunks per thread
-    static_assert((BM * 16) % NT == 0, "staging split");
-    __shared__ __attribute__((aligned(16))) uint8_t s_x[2][BM * RS];
-    __shared__ float s_rs[BM];
-
-    pin_args(a);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int lr = lane & 15, lg = lane >> 4;
-    const int wn = wave % WNW, wm = wave / WNW;
-    const int64_t M = a.M, N = a.N, K = a.K;
-    const int64_t tiles_n = (N + BN - 1) / BN, tiles_m = (M + BM - 1) / BM;
-    const int64_t ntiles = tiles_n * tiles_m;
-
-    // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
-    // of tiles (channels fastest) so its L2 shares activation rows and weights.
-    const int64_t bid = blockIdx.x;
-    const int64_t q8 = ntiles / 8, r8 = ntiles % 8;
-    const int64_t xcd = bid % 8, loc = bid / 8;
-    const int64_t tile = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
-    const int64_t n0 = (tile % tiles_n) * BN, m0 = (tile / tiles_n) * BM;
-    const int64_t S = (K + 127) / 128;
-
-    const int sc = tid & 15, srow0 = tid >> 4;
-    u32x4 xs[CPT];
-    float rsp[CPT];
-#pragma unroll
-    for (int i = 0; i < CPT; i++)
-        rsp[i] = 0.f;
-
-    // Epilogue operands, loaded now without branches and used at the end.
-    float sc_raw[FN][4];
-    uint32_t z_raw[FN][4];
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            int64_t nn = n0 + (wn * FN + fn) * 16 + 4 * lg + i;
-            nn = nn < N ? nn : N - 1;
-            sc_raw[fn][i] = a.scales[nn];
-            z_raw[fn][i] = load_zero_byte(a.zeros, a.scales, nn);
-        }
-    }
-
-    u32x4 wc[FN], wx[FN];
-    f32x4 acc[FN][FM];
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-        for (int fm = 0; fm < FM; fm++)
-            acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    auto load_w = [&](int64_t s, u32x4 *w) {
-        const int64_t k = 128 * s + 32 * lg;
-#pragma unroll
-        for (int fn = 0; fn < FN; fn++) {
-            const int64_t nn = n0 + (wn * FN + fn) * 16 + lr;
-            w[fn] = (nn < N && k < K) ? ld16(a.packed + nn * (K / 2) + k / 2) : zero4();
-        }
-    };
-    auto load_x = [&](int64_t s) {
-        const int64_t k = 128 * s + 8 * sc;
-#pragma unroll
-        for (int i = 0; i < CPT; i++) {
-            const int64_t mm = m0 + srow0 + (NT / 16) * i;
-            xs[i] = (mm < M && k < K) ? ld16(a.x + mm * K + k) : zero4();
-        }
-    };
-    auto store_x = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < CPT; i++) {
-            const int row = srow0 + (NT / 16) * i;
-            rsp[i] = sum8(xs[i], rsp[i]);
-            *reinterpret_cast<u32x4 *>(&s_x[buf][row * RS + 16 * sc]) = xs[i];
-        }
-    };
-
-    load_w(0, wc);
-    load_x(0);
-    store_x(0);
-    __syncthreads();
-    for (int64_t s = 0; s < S; s++) {
-        const int buf = (int)(s & 1);
-        const bool more = s + 1 < S;
-        if (more) {
-            load_w(s + 1, wx);
-            load_x(s + 1);
-        }
-        const uint8_t *xb = s_x[buf];
-#pragma unroll
-        for (int d = 0; d < 4; d++) {
-            u32x4 xf[FM];
-#pragma unroll
-            for (int fm = 0; fm < FM; fm++) {
-                const int row = (wm * FM + fm) * 16 + lr;
-                xf[fm] = *reinterpret_cast<const u32x4 *>(xb + row * RS + (4 * lg + d) * 16);
-            }
-#pragma unroll
-            for (int fn = 0; fn < FN; fn++) {
-                const u32x4 wa = unpack8(wc[fn][d]);
-#pragma unroll
-                for (int fm = 0; fm < FM; fm++)
-                    acc[fn][fm] = mfma16(wa, xf[fm], acc[fn][fm]);
-            }
-        }
-        if (more) {
-            store_x(buf ^ 1);
-#pragma unroll
-            for (int fn = 0; fn < FN; fn++)
-                wc[fn] = wx[fn];
-        }
-        __syncthreads();
-    }
-
-    // Per-token activation sums: 16 consecutive lanes share a row.
-#pragma unroll
-    for (int i = 0; i < CPT; i++) {
-        float v = rsp[i];
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        v += __shfl_xor(v, 4);
-        v += __shfl_xor(v, 8);
-        if (sc == 0)
-            s_rs[srow0 + (NT / 16) * i] = v;
-    }
-    __syncthreads();
-
-    // Epilogue.
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) {
-            const float sn = sc_raw[fn][i];
-            const float zc = UNPACK_OFF + zero_point(a.zeros, z_raw[fn][i]);
-#pragma unroll
-            for (int fm = 0; fm < FM; fm++) {
-                const float rsm = s_rs[(wm * FM + fm) * 16 + lr];
-                acc[fn][fm][i] = sn * __builtin_fmaf(-zc, rsm, UNPACK_SCALE * acc[fn][fm][i]);
-            }
-        }
-    }
-    if (EC) {
-        const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
-        const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
-        const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
-        int any = 0;
-#pragma unroll
-        for (int fm = 0; fm < FM; fm++) {
-            const int64_t mm = m0 + (wm * FM + fm) * 16 + lr;
-            any |= (mm < M) ? active[mm] : 0;
-        }
-        if (__ballot(any) != 0ull) {
-            const int rpad = a.rpad, r = a.r;
-            for (int t = 0; t < rpad / 32; t++) {
-                const int j = 32 * t + 8 * lg;
-                u32x4 vh[FM], vl[FM];
-#pragma unroll
-                for (int fm = 0; fm < FM; fm++) {
-                    const int64_t mm = m0 + (wm * FM + fm) * 16 + lr;
-                    vh[fm] = (mm < M) ? ld16(vhi + mm * rpad + j) : zero4();
-                    vl[fm] = (mm < M) ? ld16(vlo + mm * rpad + j) : zero4();
-                }
-#pragma unroll
-                for (int fn = 0; fn < FN; fn++) {
-                    const int64_t nn = n0 + (wn * FN + fn) * 16 + lr;
-                    const u32x4 bf = (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
-#pragma unroll
-                    for (int fm = 0; fm < FM; fm++) {
-                        acc[fn][fm] = mfma16(bf, vh[fm], acc[fn][fm]);
-                        acc[fn][fm] = mfma16(bf, vl[fm], acc[fn][fm]);
-                    }
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int fm = 0; fm < FM; fm++) {
-        const int64_t mm = m0 + (wm * FM + fm) * 16 + lr;
-        if (mm >= M)
-            continue;
-#pragma unroll
-        for (int fn = 0; fn < FN; fn++) {
-            const int64_t nb = n0 + (wn * FN + fn) * 16 + 4 * lg;
-            const f32x4 v = acc[fn][fm];
-            if (OUT_F32) {
-                float *y = reinterpret_cast<float *>(a.y) + mm * N;
-                if (nb + 3 < N && (N & 3) == 0) {
-                    *reinterpret_cast<f32x4 *>(y + nb) = v;
-                } else {
-                    for (int i = 0; i < 4; i++)
-                        if (nb + i < N)
-                            y[nb + i] = v[i];
-                }
-            } else {
-                uint16_t *y = reinterpret_cast<uint16_t *>(a.y) + mm * N;
-                if (nb + 3 < N && (N & 3) == 0) {
-                    uint2 o;
-                    o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-                    o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
-                    *reinterpret_cast<uint2 *>(y + nb) = o;
-                } else {
-                    for (int i = 0; i < 4; i++)
-                        if (nb + i < N)
-                            y[nb + i] = f2bf(v[i]);
-                }
-            }
-        }
-    }
-}
-
-template <int FN, int FM, int WNW, int WMW>
-hipError_t launch_gemm_t(const LinearArgs &a, int ec_on, hipStream_t s)
-{
-    constexpr int BN = 16 * FN * WNW, BM = 16 * FM * WMW;
-    const int64_t ntiles = ((a.N + BN - 1) / BN) * ((a.M + BM - 1) / BM);
-    const dim3 grid((unsigned)ntiles), block(64 * WNW * WMW);
-    if (ec_on) {
-        if (a.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 1, 1>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 1, 0>), grid, block, 0, s, a);
-    } else {
-        if (a.out_f32)
-            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 0, 1>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm_kernel<FN, FM, WNW, WMW, 0, 0>), grid, block, 0, s, a);
-    }
-    return hipGetLastError();
-}
-
-
-// ------------------------------------------------------------- large-M GEMM
-// Output tile 256 channels x 128 tokens, 8 waves (4 along the channels x 2
-// along the tokens), each 64 x 64 as 4 x 4 MFMA tiles.  K advances in stages
+// Output tile 256 channels x 16 FM WM tokens: WM = 2 (128 tokens, 8 waves: 4
+// along the channels x 2 along the tokens) or WM = 1 (64 tokens, 4 waves); each
+// wave holds 64 channels x 16 FM tokens as 4 x FM MFMA tiles.  K advances in stages
 // of 128.  Both operands go HBM/L2 -> LDS by global_load_lds into a ring of
 // G2_STAGES stage buffers, so the only memory operations in flight are these
 // DMAs: one stage is read while the next ones land.  Each wave waits for its
@@ -495,16 +253,16 @@ hipError_t launch_gemm_t(const LinearArgs &a, int ec_on, hipStream_t s)
 // activation sums of the offset removal come from one extra MFMA against a
 // constant-one operand per token fragment: wave column c takes the 8-deep
 // quarter c of every 32-deep step, so the extra work is spread evenly.
-constexpr int G2_WN = 4, G2_WM = 2, G2_FN = 4, G2_FM = 4;
-constexpr int G2_NT = 64 * G2_WN * G2_WM;                 // 512 threads
+//
+// Few tiles (small M): K is split into a.g_ks slices, one workgroup each, so
+// that about 256 workgroups run; a workgroup stores its scaled partial tile
+// (the EC term in slice 0 only) and a second launch (splitk_reduce_kernel)
+// adds the slices in order.  Up to 64 tokens the tile is 256 x 64 with one
+// wave per SIMD, so each weight fragment is unpacked once per workgroup.
+constexpr int G2_WN = 4, G2_FN = 4;
 constexpr int G2_BN = 16 * G2_FN * G2_WN;                 // 256 channels
-constexpr int G2_BM = 16 * G2_FM * G2_WM;                 // 128 tokens
 constexpr int G2_STAGES = 3;
-constexpr int G2_XB = G2_BM * 256;                        // activation bytes of one stage
 constexpr int G2_WB = G2_BN * 64;                         // packed weight bytes of one stage
-constexpr int G2_XI = G2_XB / (G2_NT * 16);               // activation DMAs a lane, per stage
-constexpr int G2_WI = G2_WB / (G2_NT * 16);               // weight DMAs a lane, per stage
-static_assert(G2_XI * G2_NT * 16 == G2_XB && G2_WI * G2_NT * 16 == G2_WB, "stage split");
 
 // LDS byte offsets: chunk c (0..15) of activation row r, chunk c (0..3) of weight row r.
 __device__ __forceinline__ uint32_t g2_xoff(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
@@ -520,9 +278,15 @@ __device__ __forceinline__ void lds_read4(const uint8_t *base, uint32_t a0, uint
     r3 = *reinterpret_cast<const u32x4 *>(base + a3);
 }
 
-template <int EC, int OUT_F32>
-__global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
+template <int G2_WM, int G2_FM, int SPLIT, int EC, int OUT_F32>
+__global__ __launch_bounds__(64 * G2_WN * G2_WM, 3 - G2_WM) void gemm2_kernel(const LinearArgs a)
 {
+    constexpr int G2_NT = 64 * G2_WN * G2_WM;             // 256 or 512 threads
+    constexpr int G2_BM = 16 * G2_FM * G2_WM;             // tokens
+    constexpr int G2_XB = G2_BM * 256;                    // activation bytes of one stage
+    constexpr int G2_XI = G2_XB / (G2_NT * 16);           // activation DMAs a lane, per stage
+    constexpr int G2_WI = G2_WB / (G2_NT * 16);           // weight DMAs a lane, per stage
+    static_assert(G2_XI * G2_NT * 16 == G2_XB && G2_WI * G2_NT * 16 == G2_WB, "stage split");
     __shared__ __attribute__((aligned(16))) uint8_t s_x0[G2_XB];
     __shared__ __attribute__((aligned(16))) uint8_t s_x1[G2_XB];
     __shared__ __attribute__((aligned(16))) uint8_t s_x2[G2_XB];
@@ -531,7 +295,7 @@ __global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t s_w2[G2_WB];
     __shared__ float s_rsp[G2_WN][G2_BM];     // activation-sum quarters
     static_assert(G2_STAGES == 3, "one LDS object per stage");
-    static_assert(G2_WN == 4, "one 8-deep quarter per wave column");
+    static_assert(G2_WN == 4 && G2_FN == 4, "one 8-deep quarter per wave column; 4 weight fragments");
     uint8_t *const s_xb[G2_STAGES] = {s_x0, s_x1, s_x2};
     uint8_t *const s_wb[G2_STAGES] = {s_w0, s_w1, s_w2};
 
@@ -543,15 +307,20 @@ __global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t tiles_n = (N + G2_BN - 1) / G2_BN, tiles_m = (M + G2_BM - 1) / G2_BM;
     const int64_t ntiles = tiles_n * tiles_m;
+    const int64_t KS = SPLIT ? a.g_ks : 1;
+    const int64_t nunits = ntiles * KS;                   // unit = slice * ntiles + tile
 
     // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
-    // of tiles (channels fastest) so its L2 shares activation rows and weights.
+    // of units (channels fastest, then tokens, then K slices) so its L2 shares
+    // activation rows.
     const int64_t bid = blockIdx.x;
-    const int64_t q8 = ntiles / 8, r8 = ntiles % 8;
+    const int64_t q8 = nunits / 8, r8 = nunits % 8;
     const int64_t xcd = bid % 8, loc = bid / 8;
-    const int64_t tile = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
+    const int64_t unit = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
+    const int64_t tile = unit % ntiles, ks = unit / ntiles;
     const int64_t n0 = (tile % tiles_n) * G2_BN, m0 = (tile / tiles_n) * G2_BM;
     const int64_t S = (K + 127) / 128;
+    const int64_t sb = ks * S / KS, se = (ks + 1) * S / KS;   // this slice's stages
     const uint8_t *zsrc = a.ws + a.L.zeros + 16 * (lane & 15);
 
     // DMA of one stage.  Activations: instruction j of wave w fills rows
@@ -602,27 +371,26 @@ __global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
         rsq[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // LDS addresses this lane reads (stage-relative).
-    uint32_t xoff[4][G2_FM], woff[G2_FN];
+    // Fragment fm / fn adds a whole number of 16-row blocks, which leaves the
+    // swizzles (they depend on the row modulo 16) unchanged: one base per depth
+    // step plus immediate offsets.
+    uint32_t xo[4];
 #pragma unroll
     for (int d = 0; d < 4; d++)
-#pragma unroll
-        for (int fm = 0; fm < G2_FM; fm++)
-            xoff[d][fm] = g2_xoff((wm * G2_FM + fm) * 16 + lr, 4 * lg + d);
-#pragma unroll
-    for (int fn = 0; fn < G2_FN; fn++)
-        woff[fn] = g2_woff((wn * G2_FN + fn) * 16 + lr, lg);
+        xo[d] = g2_xoff(wm * G2_FM * 16 + lr, 4 * lg + d);
+    const uint32_t wo = g2_woff(wn * G2_FN * 16 + lr, lg);
 
     // Every stage slot issues its DMAs, past the end clamped to the last stage
     // (never used), so each wave always has exactly one further stage in flight
     // when it waits for the current one.
-    const int64_t slast = S - 1;
+    const int64_t slast = se - 1;
 #pragma unroll
     for (int j = 0; j < G2_STAGES - 1; j++)
-        issue(j < slast ? j : slast, s_xb[j], s_wb[j]);
+        issue(sb + j < slast ? sb + j : slast, s_xb[j], s_wb[j]);
     constexpr int G2_WAIT = (G2_XI + G2_WI) * (G2_STAGES - 2);
     static_assert(G2_WAIT < 64, "vmcnt");
 
-    for (int64_t s0 = 0; s0 < S; s0 += G2_STAGES) {
+    for (int64_t s0 = sb; s0 < se; s0 += G2_STAGES) {
 #pragma unroll
         for (int j = 0; j < G2_STAGES; j++) {
             const int64_t s = s0 + j;
@@ -630,15 +398,16 @@ __global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
             bare_barrier();                                   // every wave's part; stage s - 1 free
             const int64_t sn = (s + G2_STAGES - 1 < slast) ? s + G2_STAGES - 1 : slast;
             issue(sn, s_xb[(j + G2_STAGES - 1) % G2_STAGES], s_wb[(j + G2_STAGES - 1) % G2_STAGES]);
-            if (s < S) {
+            if (s < se) {
                 const uint8_t *xb = s_xb[j], *wb = s_wb[j];
                 u32x4 wv[G2_FN];
-                lds_read4(wb, woff[0], woff[1], woff[2], woff[3], wv[0], wv[1], wv[2], wv[3]);
+                lds_read4(wb, wo, wo + 1024, wo + 2048, wo + 3072, wv[0], wv[1], wv[2], wv[3]);
 #pragma unroll
                 for (int d = 0; d < 4; d++) {
                     u32x4 xf[G2_FM];
-                    lds_read4(xb, xoff[d][0], xoff[d][1], xoff[d][2], xoff[d][3],
-                              xf[0], xf[1], xf[2], xf[3]);
+#pragma unroll
+                    for (int fm = 0; fm < G2_FM; fm++)
+                        xf[fm] = *reinterpret_cast<const u32x4 *>(xb + xo[d] + 4096 * fm);
                     if (d == wn) {
 #pragma unroll
                         for (int fm = 0; fm < G2_FM; fm++)
@@ -683,7 +452,7 @@ __global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
             }
         }
     }
-    if (EC) {
+    if (EC && ks == 0) {
         const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
         const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
         const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
@@ -716,6 +485,21 @@ __global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
                 }
             }
         }
+    }
+    if (SPLIT) {
+        // the scaled partial tile of this slice: unit-major, row-major bm x 256
+        float *part = reinterpret_cast<float *>(a.ws + a.L.gpart) + unit * (G2_BM * G2_BN);
+#pragma unroll
+        for (int fm = 0; fm < G2_FM; fm++) {
+            const int row = (wm * G2_FM + fm) * 16 + lr;
+            if (m0 + row >= M)
+                continue;
+#pragma unroll
+            for (int fn = 0; fn < G2_FN; fn++)
+                *reinterpret_cast<f32x4 *>(part + row * G2_BN + (wn * G2_FN + fn) * 16 + 4 * lg) =
+                    acc[fn][fm];
+        }
+        return;
     }
 #pragma unroll
     for (int fm = 0; fm < G2_FM; fm++) {
@@ -752,11 +536,82 @@ __global__ __launch_bounds__(G2_NT) void gemm2_kernel(const LinearArgs a)
     }
 }
 
-template <int EC, int OUT_F32>
+// Second launch of a K-split GEMM: y = the sum of the slices' partial tiles in
+// slice order; a thread takes 4 consecutive channels of one token.
+template <int OUT_F32>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
+{
+    const int64_t M = a.M, N = a.N, KS = a.g_ks, bm = a.g_bm;
+    const int64_t nq = (N + 3) / 4;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * nq)
+        return;
+    const int64_t m = idx / nq, n = 4 * (idx % nq);
+    const int64_t tiles_n = (N + G2_BN - 1) / G2_BN, ntiles = tiles_n * ((M + bm - 1) / bm);
+    const int64_t tile = (m / bm) * tiles_n + n / G2_BN;
+    const int64_t off = (m % bm) * G2_BN + n % G2_BN;
+    const f32x4 *part = reinterpret_cast<const f32x4 *>(a.ws + a.L.gpart);
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
+        f32x4 p[CMB_U];
+#pragma unroll
+        for (int i = 0; i < CMB_U; i++)
+            if (q0 + i < KS)
+                p[i] = part[(((q0 + i) * ntiles + tile) * bm * G2_BN + off) / 4];
+#pragma unroll
+        for (int i = 0; i < CMB_U; i++)
+            if (q0 + i < KS)
+                v += p[i];
+    }
+    if (OUT_F32) {
+        float *y = reinterpret_cast<float *>(a.y) + m * N;
+        if (n + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<f32x4 *>(y + n) = v;
+        } else {
+            for (int i = 0; i < 4; i++)
+                if (n + i < N)
+                    y[n + i] = v[i];
+        }
+    } else {
+        uint16_t *y = reinterpret_cast<uint16_t *>(a.y) + m * N;
+        if (n + 3 < N && (N & 3) == 0) {
+            uint2 o;
+            o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+            o.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+            *reinterpret_cast<uint2 *>(y + n) = o;
+        } else {
+            for (int i = 0; i < 4; i++)
+                if (n + i < N)
+                    y[n + i] = f2bf(v[i]);
+        }
+    }
+}
+
+template <int WM, int FM, int EC>
 hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
 {
-    const int64_t ntiles = ((a.N + G2_BN - 1) / G2_BN) * ((a.M + G2_BM - 1) / G2_BM);
-    hipLaunchKernelGGL((gemm2_kernel<EC, OUT_F32>), dim3((unsigned)ntiles), dim3(G2_NT), 0, s, a);
+    const int64_t bm = 16 * FM * WM;
+    const int64_t ntiles = ((a.N + G2_BN - 1) / G2_BN) * ((a.M + bm - 1) / bm);
+    const dim3 block(64 * G2_WN * WM);
+    if (a.g_ks > 1) {
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1>), dim3((unsigned)(ntiles * a.g_ks)),
+                           block, 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+        const int64_t threads = a.M * ((a.N + 3) / 4);
+        if (a.out_f32)
+            hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3((unsigned)((threads + 255) / 256)),
+                               dim3(256), 0, s, a);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3((unsigned)((threads + 255) / 256)),
+                               dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    if (a.out_f32)
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1>), dim3((unsigned)ntiles), block, 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0>), dim3((unsigned)ntiles), block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -778,13 +633,10 @@ hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 
 hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStream_t s)
 {
-    if (!force_large && a.M <= 64)
-        return launch_gemm_t<2, 2, 2, 2>(a, ec_on, s);   // 64 x 64 tiles
-    if (!force_large && a.M * a.N < 256 * 128 * 256)     // too few 256 x 128 tiles to fill the chip
-        return launch_gemm_t<4, 4, 2, 2>(a, ec_on, s);   // 128 x 128 tiles
-    if (ec_on)
-        return a.out_f32 ? launch_gemm2_t<1, 1>(a, s) : launch_gemm2_t<1, 0>(a, s);
-    return a.out_f32 ? launch_gemm2_t<0, 1>(a, s) : launch_gemm2_t<0, 0>(a, s);
+    (void)force_large;                                    // a.g_bm and a.g_ks carry the choice
+    if (a.g_bm == 64)
+        return ec_on ? launch_gemm2_t<1, 4, 1>(a, s) : launch_gemm2_t<1, 4, 0>(a, s);
+    return ec_on ? launch_gemm2_t<2, 4, 1>(a, s) : launch_gemm2_t<2, 4, 0>(a, s);
 }
 
 } // namespace spear
