@@ -10,34 +10,39 @@
 //
 // Work decomposition (one launch):
 //  * a workgroup owns 16 output channels and a K range (all of K unless the
-//    activations of the range would not fit in LDS).  Its 4 stream waves load
-//    the activations of the range straight into LDS (global_load_lds), then
-//    issue every 16-byte load of their packed-weight share (HBM -> registers)
-//    and contract on bf16 MFMA as each load lands (the packed word order makes
-//    the unpacked pairs line up with the activations' own pairs), with the
-//    tokens (padded to 16) as the MFMA's N side.  A second MFMA against a constant-one operand gives the per-token
-//    activation sums that remove the unpack offset in the epilogue.
+//    activations of the range would not fit in LDS).  Each of its 4 stream
+//    waves owns a run of 128-deep super-steps: it DMAs the activations of
+//    exactly those steps into LDS (global_load_lds), issues every 16-byte load
+//    of its packed-weight share (HBM -> registers), and contracts each step as
+//    its load lands -- no workgroup barrier before the contraction.  Several
+//    tokens: bf16 MFMA with the tokens (padded to 16) on the MFMA's N side and
+//    a second MFMA against a constant-one operand for the per-token activation
+//    sums that remove the unpack offset.  One token: a wavefront-reduction
+//    GEMV (bf16 dot2 into fp32, four accumulators) and a VALU activation sum.
+//    The packed word order makes the unpacked pairs line up with the
+//    activations' own pairs, so the activations are used as loaded.
 //  * When K is split over workgroups, the last one of a channel group (atomic
 //    counter) sums the partial tiles in slice order (deterministic).
 //  * EC (fused mode): the lowest block indices, which the dispatcher places
-//    first, are `nprod` producer workgroups.  Each reads about 16 KB of A (so a
-//    producer's share of the memory system is no larger than a stream
-//    workgroup's and its result is ready before the stream ends), computes
-//    the gate-logit partial (fp64) and A.x (MFMA) of every token over its K
-//    slice, reduces its 4 waves in LDS and stores the partials as 64-bit words
-//    {value, launch epoch}, one relaxed device-coherent store each, then
-//    leaves.  The epilogue workgroup of each channel group loads the words of
-//    its tokens (relaxed device-coherent loads, the 4 waves splitting the
-//    producers), re-loads until every tag carries this launch's epoch
-//    (bounded), sums the producers in order, applies the gate and the
-//    hard-gate selection, forms v = g (A x) as bf16 hi + lo and adds B v with
-//    two MFMAs per 32 ranks.  Each word is validated on its own, so no fence
-//    or counter orders the exchange; every epilogue computes the same v in
-//    the same order, and producers never wait.
-//  * The launch epoch comes from a 64-bit counter in the workspace: block 0
-//    adds 2^32 - (grid - 1) and every other block adds 1, so a launch adds
-//    exactly 2^32 whatever its grid, and every block of the launch reads the
-//    same upper half.  Graph replays and calls of other shapes on the same
+//    first, are `nprod` producer workgroups.  Each reads about 16 KB of A per
+//    pair of tokens (so a producer's share of the memory system is no larger
+//    than a stream workgroup's and its result is ready before the stream
+//    ends), computes the gate-logit partial (fp64) and A.x (MFMA; dot2 for one
+//    token) of every token over its K slice, reduces its 4 waves in LDS and
+//    stores the partials as 64-bit words {value, launch epoch}, one relaxed
+//    device-coherent store each, then leaves.  The epilogue of each channel
+//    group loads the words of its tokens (relaxed device-coherent loads, the 4
+//    waves splitting the producers), re-loads until every tag carries this
+//    launch's epoch (bounded), sums the producers in order, applies the gate
+//    and the hard-gate selection, forms v = g (A x) as bf16 hi + lo and adds
+//    B v (two MFMAs per 32 ranks; dot2 for one token).  Each word is validated
+//    on its own, so no fence or counter orders the exchange; every epilogue
+//    computes the same v in the same order, and producers never wait.
+//  * The launch epoch comes from 64 counters in the workspace, 128 bytes
+//    apart; block b adds to counter b % 64 so that no address is contended by
+//    more than a few workgroups.  A launch adds exactly 2^32 to every counter
+//    whatever its grid (see epoch_claim), and every block of the launch reads
+//    the same upper half.  Graph replays and calls of other shapes on the same
 //    workspace therefore never see a stale tag as current.
 #include "spear_internal.hpp"
 
