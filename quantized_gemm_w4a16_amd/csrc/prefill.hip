@@ -279,7 +279,7 @@ __device__ __forceinline__ void lds_read4(const uint8_t *base, uint32_t a0, uint
 }
 
 template <int G2_WM, int G2_FM, int SPLIT, int EC, int OUT_F32>
-__global__ __launch_bounds__(64 * G2_WN * G2_WM, 3 - G2_WM) void gemm2_kernel(const LinearArgs a)
+__global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearArgs a)
 {
     constexpr int G2_NT = 64 * G2_WN * G2_WM;             // 256 or 512 threads
     constexpr int G2_BM = 16 * G2_FM * G2_WM;             // tokens
@@ -328,36 +328,69 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM, 3 - G2_WM) void gemm2_kernel(co
     // (row % 16) of its row); rows past M repeat row M - 1 (never stored).
     // Weights: instruction j fills rows 16 (G2_WI w + j) .. +15, lane i the slot
     // i of that 1 KB (chunk (i % 4) ^ ((row / 2) % 4)); rows past N repeat the
-    // last row.
+    // last row.  Each lane's stage-0 source and the number of stages its chunk
+    // stays inside K are computed once.  Activation chunks past K come from the
+    // zero block; weight chunks past K re-read the lane's last chunk inside K
+    // (finite values that meet zero activations).
+    const uint8_t *xsrc[G2_XI], *wsrc[G2_WI];
+    int64_t xlim[G2_XI], wlast[G2_WI];
+#pragma unroll
+    for (int j = 0; j < G2_XI; j++) {
+        const int r = 4 * (G2_XI * wave + j) + (lane >> 4);
+        const int c = (lane & 15) ^ (r & 15);
+        const int64_t mm = m0 + r < M ? m0 + r : M - 1;
+        xsrc[j] = reinterpret_cast<const uint8_t *>(a.x + mm * K + 8 * c);
+        xlim[j] = (K - 8 * c + 127) / 128;                // stages st with 128 st + 8 c < K
+    }
+#pragma unroll
+    for (int j = 0; j < G2_WI; j++) {
+        const int r = 16 * (G2_WI * wave + j) + (lane >> 2);
+        const int c = (lane & 3) ^ ((r >> 1) & 3);
+        const int64_t nn = n0 + r < N ? n0 + r : N - 1;
+        wsrc[j] = a.packed + nn * (K / 2) + 16 * c;
+        wlast[j] = (K - 32 * c + 127) / 128 - 1;          // last stage with 128 st + 32 c < K
+    }
     auto issue = [&](int64_t st, uint8_t *xbase, uint8_t *wbase) {
 #pragma unroll
         for (int j = 0; j < G2_XI; j++) {
-            const int r0 = 4 * (G2_XI * wave + j);
-            const int r = r0 + (lane >> 4);
-            const int c = (lane & 15) ^ (r & 15);
-            const int64_t k = 128 * st + 8 * c;
-            int64_t mm = m0 + r;
-            mm = mm < M ? mm : M - 1;
-            const void *src = (k < K) ? (const void *)(a.x + mm * K + k) : (const void *)zsrc;
+            const void *src = st < xlim[j] ? (const void *)(xsrc[j] + 256 * st) : (const void *)zsrc;
             __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(xbase + r0 * 256),
+                                             (__attribute__((address_space(3))) void *)(xbase + 1024 * (G2_XI * wave + j)),
                                              16, 0, 0);
         }
 #pragma unroll
         for (int j = 0; j < G2_WI; j++) {
-            const int r0 = 16 * (G2_WI * wave + j);
-            const int r = r0 + (lane >> 2);
-            const int c = (lane & 3) ^ ((r >> 1) & 3);
-            const int64_t k = 128 * st + 32 * c;
-            int64_t nn = n0 + r;
-            nn = nn < N ? nn : N - 1;
-            const void *src = (k < K) ? (const void *)(a.packed + nn * (K / 2) + k / 2)
-                                      : (const void *)zsrc;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(wbase + r0 * 64),
+            const int64_t sw = st < wlast[j] ? st : wlast[j];
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(wsrc[j] + 64 * sw),
+                                             (__attribute__((address_space(3))) void *)(wbase + 1024 * (G2_WI * wave + j)),
                                              16, 0, 0);
         }
     };
+
+    // EC operands of one 32-rank chunk t: v (hi, lo) of this wave's tokens and
+    // B rows of its channels.  With one wave per SIMD there is room to load the
+    // slice's first chunk now, so its round trip overlaps the main loop.
+    auto ec_load = [&](int t, u32x4 *vh, u32x4 *vl, u32x4 *bf) {
+        const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
+        const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
+        const int rpad = a.rpad, r = a.r;
+        const int j = 32 * t + 8 * lg;
+#pragma unroll
+        for (int fm = 0; fm < G2_FM; fm++) {
+            const int64_t mm = m0 + (wm * G2_FM + fm) * 16 + lr;
+            vh[fm] = (mm < M) ? ld16(vhi + mm * rpad + j) : zero4();
+            vl[fm] = (mm < M) ? ld16(vlo + mm * rpad + j) : zero4();
+        }
+#pragma unroll
+        for (int fn = 0; fn < G2_FN; fn++) {
+            const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
+            bf[fn] = (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
+        }
+    };
+    constexpr bool ECPRE = EC && G2_WM == 1;
+    u32x4 pvh[G2_FM], pvl[G2_FM], pbf[G2_FN];
+    if (ECPRE && ks < a.rpad / 32)
+        ec_load((int)ks, pvh, pvl, pbf);
 
     f32x4 acc[G2_FN][G2_FM], rsq[G2_FM];
     const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -452,10 +485,10 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM, 3 - G2_WM) void gemm2_kernel(co
             }
         }
     }
-    if (EC && ks == 0) {
+    if (EC && ks < a.rpad / 32) {
+        // Rank chunks of 32: slice ks takes chunks ks, ks + KS, ... (the
+        // second launch adds the slices), so a K split also splits the EC.
         const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
-        const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
-        const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
         int any = 0;
 #pragma unroll
         for (int fm = 0; fm < G2_FM; fm++) {
@@ -463,26 +496,27 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM, 3 - G2_WM) void gemm2_kernel(co
             any |= (mm < M) ? active[mm] : 0;
         }
         if (__ballot(any) != 0ull) {
-            const int rpad = a.rpad, r = a.r;
-            for (int t = 0; t < rpad / 32; t++) {
-                const int j = 32 * t + 8 * lg;
-                u32x4 vh[G2_FM], vl[G2_FM];
-#pragma unroll
-                for (int fm = 0; fm < G2_FM; fm++) {
-                    const int64_t mm = m0 + (wm * G2_FM + fm) * 16 + lr;
-                    vh[fm] = (mm < M) ? ld16(vhi + mm * rpad + j) : zero4();
-                    vl[fm] = (mm < M) ? ld16(vlo + mm * rpad + j) : zero4();
-                }
-#pragma unroll
-                for (int fn = 0; fn < G2_FN; fn++) {
-                    const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
-                    const u32x4 bf = (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
+            for (int64_t t = ks; t < a.rpad / 32; t += KS) {
+                u32x4 vh[G2_FM], vl[G2_FM], bf[G2_FN];
+                if (ECPRE && t == ks) {
 #pragma unroll
                     for (int fm = 0; fm < G2_FM; fm++) {
-                        acc[fn][fm] = mfma16(bf, vh[fm], acc[fn][fm]);
-                        acc[fn][fm] = mfma16(bf, vl[fm], acc[fn][fm]);
+                        vh[fm] = pvh[fm];
+                        vl[fm] = pvl[fm];
                     }
+#pragma unroll
+                    for (int fn = 0; fn < G2_FN; fn++)
+                        bf[fn] = pbf[fn];
+                } else {
+                    ec_load((int)t, vh, vl, bf);
                 }
+#pragma unroll
+                for (int fn = 0; fn < G2_FN; fn++)
+#pragma unroll
+                    for (int fm = 0; fm < G2_FM; fm++) {
+                        acc[fn][fm] = mfma16(bf[fn], vh[fm], acc[fn][fm]);
+                        acc[fn][fm] = mfma16(bf[fn], vl[fm], acc[fn][fm]);
+                    }
             }
         }
     }
