@@ -34,10 +34,13 @@
 //    group loads the words of its tokens (relaxed device-coherent loads, the 4
 //    waves splitting the producers), re-loads until every tag carries this
 //    launch's epoch (bounded), sums the producers in order, applies the gate
-//    and the hard-gate selection, forms v = g (A x) as bf16 hi + lo and adds
-//    B v (two MFMAs per 32 ranks; dot2 for one token).  Each word is validated
-//    on its own, so no fence or counter orders the exchange; every epilogue
-//    computes the same v in the same order, and producers never wait.
+//    and the hard-gate selection, and adds g B (A x): B times A x as bf16
+//    hi + lo (two MFMAs per 32 ranks; dot2 for one token), scaled by the gate
+//    at the end so the fp64 sigmoid is off the MFMAs' path.  The first batch
+//    of words is in flight while wave 0 reduces the stream waves.  Each word
+//    is validated on its own, so no fence or counter orders the exchange;
+//    every epilogue sums the same partials in the same order, and producers
+//    never wait.
 //  * The launch epoch comes from 64 counters in the workspace, 128 bytes
 //    apart; block b adds to counter b % 64 so that no address is contended by
 //    more than a few workgroups.  A launch adds exactly 2^32 to every counter
@@ -54,6 +57,7 @@ constexpr int DEC_THREADS = 64 * DEC_WAVES;               // stream waves
 
 struct DecShared {
     float red[DEC_WAVES][64][5];
+    alignas(16) float red16[DEC_WAVES][16];   // one token: each wave's channel sums
     float xs[DEC_WAVES];        // one token: the activation sum of each wave's chunks
     uint32_t u32[4];
 };
@@ -302,15 +306,17 @@ __device__ void ec_produce_gv(const LinearArgs &a, int64_t p, int wave, int lane
 // lanes, consecutive words) of 8 / KM producers, and the gate-logit words of
 // token l % 16 of producer l / 16 (+ 4); a batch is re-loaded until every tag is
 // this launch's.  The wave subtotals meet in LDS and wave 0 finishes.  KM is
-// ceil(M / 2) rounded up to a power of two.  With GV (one token) B v is taken
+// ceil(M / 2) rounded up to a power of two.  `overlap` runs once in every wave,
+// while the wave's first batch is in flight.  B u is formed first and the
+// gate (act g) scales it at the end.  With GV (one token) B u is taken
 // on the vector ALU in fp32: lane (c, g) forms the partial of channel c over
 // ranks 8 g .. 8 g + 7, the four partials meet by shuffles in order, and each
 // lane then picks its four output channels.  Returns, in wave 0, e[i] for
 // channel 16 cg + 4 lg + i and token lr; *ok_out is false (and the term zero)
 // when a bounded wait expired.  Writes the gate outputs when cg == 0.
-template <int KM, int GV>
+template <int KM, int GV, typename F>
 __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, int wave, int lane,
-                            uint8_t *lds, uint32_t tag, bool *ok_out)
+                            uint8_t *lds, uint32_t tag, bool *ok_out, F overlap)
 {
     constexpr int SPB = 8 / KM;                             // producers per batch
     const int lr = lane & 15, lg = lane >> 4;
@@ -333,7 +339,7 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
     f32x4 e = {0.f, 0.f, 0.f, 0.f};
     float g = 0.f;
     int act = 0;
-    bool ok = true;
+    bool ok = true, overlapped = false;
     for (int t = 0; t < rpad / 32; t++) {
         float us[KM];
 #pragma unroll
@@ -359,6 +365,10 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                         wz[j][0] = load_tagged(pz + (pp * 16 + zm) * 2);
                         wz[j][1] = load_tagged(pz + (pp * 16 + zm) * 2 + 1);
                     }
+                }
+                if (t == 0 && pc == p0 && it == 0) {
+                    overlap();                              // runs while the first words fly
+                    overlapped = true;
                 }
 #pragma unroll
                 for (int c = 0; c < SPB; c++)
@@ -396,6 +406,10 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                                                               ((uint64_t)(uint32_t)wz[j][1] << 32));
             }
         }
+        if (!overlapped) {                                  // no producers in this wave, or a timeout
+            overlap();
+            overlapped = true;
+        }
 #pragma unroll
         for (int k = 0; k < KM; k++)
             if (rh + 2 * k < 16)
@@ -430,9 +444,8 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                 }
             }
             if constexpr (GV) {
-                // token 0's u[32 t + 8 lg + q], q = 0..7; lanes of other tokens drop out
-                const float g0 = __shfl(g, 0);
-                const int act0 = __shfl(act, 0);
+                // token 0's u[32 t + 8 lg + q], q = 0..7; lanes of other tokens drop
+                // out.  B u first; the gate scales the sum at the end.
                 f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua;
 #pragma unroll
                 for (int w = 0; w < DEC_WAVES; w++) {
@@ -448,7 +461,7 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                 float ep = 0.f;
 #pragma unroll
                 for (int q = 0; q < 8; q++) {
-                    const float v = act0 ? g0 * (q < 4 ? ua[q] : ub[q - 4]) : 0.f;
+                    const float v = q < 4 ? ua[q] : ub[q - 4];
                     const uint32_t bw = bf[q / 2];
                     const float bq = __uint_as_float((q & 1) ? (bw & 0xFFFF0000u) : (bw << 16));
                     ep = __builtin_fmaf(bq, v, ep);
@@ -461,7 +474,8 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                 for (int i = 0; i < 4; i++)
                     e[i] += __shfl(erow, 4 * lg + i);
             } else {
-                // u[lr][32 t + 8 lg + q]; rows >= M hold stale LDS and are not active
+                // u[lr][32 t + 8 lg + q]; rows >= M hold stale LDS and are zeroed.
+                // B u first (hi + lo); the gate scales the sum at the end.
                 f32x4 ua = {0.f, 0.f, 0.f, 0.f}, ub = ua;
 #pragma unroll
                 for (int w = 0; w < DEC_WAVES; w++) {
@@ -472,8 +486,8 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                 u32x4 vh, vl;
 #pragma unroll
                 for (int q = 0; q < 4; q++) {
-                    const float v0 = act ? g * (q < 2 ? ua[2 * q] : ub[2 * q - 4]) : 0.f;
-                    const float v1 = act ? g * (q < 2 ? ua[2 * q + 1] : ub[2 * q - 3]) : 0.f;
+                    const float v0 = lr < M ? (q < 2 ? ua[2 * q] : ub[2 * q - 4]) : 0.f;
+                    const float v1 = lr < M ? (q < 2 ? ua[2 * q + 1] : ub[2 * q - 3]) : 0.f;
                     const uint16_t h0 = f2bf(v0), h1 = f2bf(v1);
                     vh[q] = (uint32_t)h0 | ((uint32_t)h1 << 16);
                     vl[q] = (uint32_t)f2bf(v0 - bf16f(h0)) | ((uint32_t)f2bf(v1 - bf16f(h1)) << 16);
@@ -493,8 +507,10 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
             break;
         }
     }
+    // the gate of the lane's token (token 0 with one token)
+    const float gs = GV ? (__shfl(act, 0) ? __shfl(g, 0) : 0.f) : (act ? g : 0.f);
     *ok_out = ok;
-    return ok ? e : f32x4{0.f, 0.f, 0.f, 0.f};
+    return ok ? e * gs : f32x4{0.f, 0.f, 0.f, 0.f};
 }
 
 template <int EC_MODE, int OUT_F32, int SW, int GV>
@@ -644,7 +660,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
                 }
             }
         }
-        sh.red[wave][lane][0] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        // the wave's four lane groups (k quarters of every step) of channel c
+        float v = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (lane < 16)
+            sh.red16[wave][lane] = v;
     } else {
         f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0, rs0 = acc0, rs1 = acc0;
         const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -681,78 +702,85 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     //    wave 0 holds channels n0 + 4 g + i of token t, and token t's sum of x.
     f32x4 tot = {0.f, 0.f, 0.f, 0.f};
     float rst = 0.f;
-    if (GV && wave == 0) {
-        for (int w = 0; w < DEC_WAVES; w++) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                const int c = 4 * lg + i;
-                tot[i] += ((sh.red[w][c][0] + sh.red[w][c + 16][0]) + sh.red[w][c + 32][0]) +
-                          sh.red[w][c + 48][0];
+    auto reduce_waves = [&]() {
+        if (GV && wave == 0) {
+            for (int w = 0; w < DEC_WAVES; w++) {
+                tot += *reinterpret_cast<const f32x4 *>(&sh.red16[w][4 * lg]);
+                rst += sh.xs[w];
             }
-            rst += sh.xs[w];
-        }
-    } else if (wave == 0) {
-        for (int w = 0; w < DEC_WAVES; w++) {
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                tot[i] += sh.red[w][lane][i];
-            rst += sh.red[w][lane][4];
-        }
-    }
-
-    // 8. Reduce the K ranges: the last workgroup of the channel group sums them in order.
-    bool epi = true;
-    if (ksplit > 1) {
-        float *splitp = reinterpret_cast<float *>(a.ws + a.L.splitp);
-        uint32_t *colcnt = reinterpret_cast<uint32_t *>(a.ws + a.L.colcnt);
-        if (wave == 0) {
-            if (lr < M) {
-                float *pp = splitp + ((cg * ksplit + ks) * 64 + lane) * 5;
+        } else if (wave == 0) {
+            for (int w = 0; w < DEC_WAVES; w++) {
 #pragma unroll
                 for (int i = 0; i < 4; i++)
-                    pp[i] = tot[i];
-                pp[4] = rst;
-            }
-            release_agent();
-            if (lane == 0)
-                sh.u32[1] = __hip_atomic_fetch_add(&colcnt[cg], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();
-        epi = sh.u32[1] == (uint32_t)(ksplit - 1);
-        if (epi && wave == 0) {
-            acquire_agent();
-            if (lane == 0)
-                atomic_store_relaxed(&colcnt[cg], 0u);
-            tot = f32x4{0.f, 0.f, 0.f, 0.f};
-            rst = 0.f;
-            if (lr < M) {
-                for (int64_t q = 0; q < ksplit; q++) {
-                    const float *pp = splitp + ((cg * ksplit + q) * 64 + lane) * 5;
-#pragma unroll
-                    for (int i = 0; i < 4; i++)
-                        tot[i] += pp[i];
-                    rst += pp[4];
-                }
+                    tot[i] += sh.red[w][lane][i];
+                rst += sh.red[w][lane][4];
             }
         }
-    }
+    };
 
-    // 9. Epilogue: the EC term (fused mode: all 4 waves), then wave 0 scales,
-    //    removes the offset, adds the EC term and stores.
+    // 9 (fused EC). The EC term, all 4 waves; the wave reduction above runs
+    // while the first partial words are in flight when K is not split.
     f32x4 ec_e = {0.f, 0.f, 0.f, 0.f};
-    if (EC_MODE == 1 && epi) {
+    auto consume = [&](auto overlap) {
         bool ok;
         const uint32_t tag = sh.u32[0];
         if (M <= 2)
-            ec_e = ec_consume<1, (GV && 1 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<1, (GV && 1 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok, overlap);
         else if (M <= 4)
-            ec_e = ec_consume<2, (GV && 2 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<2, (GV && 2 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok, overlap);
         else if (M <= 8)
-            ec_e = ec_consume<4, (GV && 4 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<4, (GV && 4 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok, overlap);
         else
-            ec_e = ec_consume<8, (GV && 8 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok);
+            ec_e = ec_consume<8, (GV && 8 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok, overlap);
+    };
+
+    bool epi = true;
+    if (EC_MODE == 1 && ksplit == 1) {
+        consume(reduce_waves);
+    } else {
+        reduce_waves();
+
+        // 8. Reduce the K ranges: the last workgroup of the channel group sums them in order.
+        if (ksplit > 1) {
+            float *splitp = reinterpret_cast<float *>(a.ws + a.L.splitp);
+            uint32_t *colcnt = reinterpret_cast<uint32_t *>(a.ws + a.L.colcnt);
+            if (wave == 0) {
+                if (lr < M) {
+                    float *pp = splitp + ((cg * ksplit + ks) * 64 + lane) * 5;
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        pp[i] = tot[i];
+                    pp[4] = rst;
+                }
+                release_agent();
+                if (lane == 0)
+                    sh.u32[1] = __hip_atomic_fetch_add(&colcnt[cg], 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            __syncthreads();
+            epi = sh.u32[1] == (uint32_t)(ksplit - 1);
+            if (epi && wave == 0) {
+                acquire_agent();
+                if (lane == 0)
+                    atomic_store_relaxed(&colcnt[cg], 0u);
+                tot = f32x4{0.f, 0.f, 0.f, 0.f};
+                rst = 0.f;
+                if (lr < M) {
+                    for (int64_t q = 0; q < ksplit; q++) {
+                        const float *pp = splitp + ((cg * ksplit + q) * 64 + lane) * 5;
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            tot[i] += pp[i];
+                        rst += pp[4];
+                    }
+                }
+            }
+        }
+        if (EC_MODE == 1 && epi)
+            consume([] {});
     }
+
+    // 10. Wave 0 scales, removes the offset, adds the EC term and stores.
     if (epi && wave == 0) {
         float yv[4];
 #pragma unroll
