@@ -192,7 +192,10 @@ def random_case(M, N, K, r, kind, hard, seed):
 
 RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 256),
           (17, 1000, 160, 40), (33, 24, 4096, 8), (100, 200, 544, 64), (130, 129, 1024, 32),
-          (257, 300, 2080, 24), (200, 300, 352, 32), (129, 513, 192, 16)]
+          (257, 300, 2080, 24), (200, 300, 352, 32), (129, 513, 192, 16),
+          # K split over workgroups with a K tail and EC rank chunks spread over
+          # the slices, on both sides of the 64-token tile switch
+          (64, 260, 1184, 96), (65, 700, 1280, 48)]
 
 
 @pytest.mark.parametrize("M,N,K,r", RAGGED)
