@@ -125,12 +125,12 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
         off = align256(off + (size_t)(L.mpad * L.rpad) * 2);
         L.active = off;
         off = align256(off + (size_t)L.mpad * 4);
-        // EC pre-pass with K split over workgroups: per-slot partials (sized
-        // independently of M).
+        // EC pre-pass with K split over workgroups: per-slot partials as tagged
+        // 64-bit words (sized independently of M).
         L.preu = off;
-        off = align256(off + (size_t)PRE_SLOTS * 16 * L.rpad * sizeof(float));
+        off = align256(off + (size_t)PRE_SLOTS * 16 * L.rpad * sizeof(uint64_t));
         L.prez = off;
-        off = align256(off + (size_t)PRE_SLOTS * 16 * sizeof(double));
+        off = align256(off + (size_t)PRE_SLOTS * 16 * 2 * sizeof(uint64_t));
     }
     L.gpart = off;
     off = align256(off + gemm_part_bytes(M, N, K));
@@ -352,8 +352,8 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
     a.prod_k = L.prod_k;
     a.mpad = L.mpad;
     {
-        // EC pre-pass: few token groups split K so that about 256 workgroups
-        // run, each over at least 8 steps of 32.
+        // EC pre-pass: few token groups split K so that up to about 256
+        // workgroups run, each over at least 8 steps of 32 (one per wave).
         const int64_t tg = cdiv(M > 0 ? M : 1, 16), T = K / 32;
         int64_t ks = 1;
         if (tg < PRE_GROUPS) {

@@ -84,52 +84,6 @@ static_assert(EC_LDS_U >= DEC_WAVES * 16 * 32 * sizeof(float), "consumer u excha
 constexpr size_t EC_LDS_Z = DEC_WAVES * 64 * sizeof(double);      // gate-logit partials
 constexpr size_t EC_LDS = EC_LDS_U + EC_LDS_Z + 64;               // + tag and flags
 
-// One atomic add per workgroup.  Block b claims on counter b % EPOCH_CTRS and
-// a launch adds exactly 2^32 to every counter: the first block of each class
-// adds 2^32 - (n - 1), the n - 1 others of the class 1 each, and block 0 adds
-// 2^32 to the counters no block of a small grid uses.  Between launches all
-// counters hold the same multiple of 2^32, so every block of a launch reads the
-// same upper half whatever the order of the adds.
-__device__ __forceinline__ uint64_t epoch_claim(const LinearArgs &a)
-{
-    uint8_t *base = a.ws + a.L.epoch;
-    const uint32_t G = gridDim.x, bid = blockIdx.x, c = bid % EPOCH_CTRS;
-    uint64_t add = 1;
-    if (bid < EPOCH_CTRS)
-        add = (1ull << 32) - ((G - 1 - c) / EPOCH_CTRS + 1) + 1;
-    if (bid == 0)
-        for (uint32_t cc = G; cc < EPOCH_CTRS; cc++)
-            __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(base + (size_t)cc * EPOCH_STRIDE),
-                                   1ull << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return __hip_atomic_fetch_add(reinterpret_cast<uint64_t *>(base + (size_t)c * EPOCH_STRIDE), add,
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Tag of the launch (a zeroed workspace holds tag 0, which no launch uses).
-__device__ __forceinline__ uint32_t epoch_tag(uint64_t claimed) { return (uint32_t)(claimed >> 32) + 1u; }
-
-// A zero the compiler cannot see through.  The epoch claim returns into two
-// registers long before its value is used; with a literal zero on the other
-// path the tag arithmetic is folded (or hoisted) to right behind the atomic,
-// and a dead low half lets its register be reused, and each of these makes the
-// wave wait for the atomic and every older load there.  Adding this opaque
-// zero at the use keeps the arithmetic, and both registers, where they belong.
-__device__ __forceinline__ uint64_t opaque_zero64()
-{
-    uint32_t lo, hi;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(lo));
-    asm volatile("v_mov_b32 %0, 0" : "=v"(hi));
-    return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ void store_tagged(uint64_t *p, uint32_t bits, uint32_t tag)
-{
-    __hip_atomic_store(p, ((uint64_t)tag << 32) | bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t load_tagged(const uint64_t *p)
-{
-    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Producer workgroup p: wave w takes K slice [(4p + w) prod_k, +prod_k) and
 // computes, for all 16 token slots, the gate-logit partial (fp64) and
 // u[m][j] = sum_k A[j][k] x[m][k] (MFMA, fp32).  The waves are summed in order

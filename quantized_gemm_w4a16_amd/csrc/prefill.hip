@@ -22,16 +22,22 @@ namespace {
 // A).  A wave walks its part in chunks of PRE_T 32-deep steps and, per chunk,
 // issues every load (x, up to PRE_RT 16-rank tiles of A, w_g) before it uses
 // any, so one memory round trip covers the chunk.  With one slice the
-// workgroup finishes the tokens itself; with several it stores its partials in
-// the workspace and a second launch (prepass_combine) sums the slices of each
-// group in order and finishes them.  (A release fence and counter inside one
-// launch would instead write back the whole L2 once per workgroup.)
+// workgroup finishes the tokens itself.  With several, every workgroup but the
+// group's last slice stores its partials as tagged words {value, launch epoch}
+// (relaxed device-coherent stores), and the last slice -- the group's highest
+// block index, dispatched after the others, which never wait -- re-loads the
+// other slices' words until every tag is this launch's (bounded; an expired
+// wait drops the group's EC term and is counted), adds the slices in order
+// and finishes the tokens.  Each word is validated on its own, so no fence or
+// counter is involved (a release fence per workgroup would write back the
+// whole L2).
 constexpr int PRE_WAVES = 8;
 constexpr int PRE_T = 8;                       // 32-deep steps per chunk
 constexpr int PRE_RT = 4;                      // 16-rank tiles per pass over the slice
 constexpr int PRE_TILES = SPEAR_MAX_RANK / 16;
-constexpr int CMB_WAVES = 4;                   // combine: waves over the u tiles (one more sums z)
-constexpr int CMB_U = 16;                      // slot loads a combine thread has in flight
+constexpr int PRE_FE = 2;                      // finisher: u elements a thread adds up per batch
+constexpr int PRE_FQ = 16;                     // finisher: slices per batch (loads in flight)
+constexpr int CMB_U = 16;                      // split-K reduction: slice loads in flight
 
 // The last step of the pre-pass for tokens m0 .. m0 + 15, given their logit
 // sums (without b) in s_zw and u in s_uw (tile t, lane l: ranks 16 t + 4 (l / 16)
@@ -90,10 +96,14 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
     __shared__ double s_zw[16];
     __shared__ float s_g[16];
     __shared__ int s_act[16];
+    __shared__ uint32_t s_tag, s_bad;
     pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, K = a.K, KS = a.pre_ks;
+    uint64_t claimed = opaque_zero64();
+    if (KS > 1 && tid == 0)
+        claimed = epoch_claim(a);                         // back long before it is used
     const int64_t grp = blockIdx.x / KS, ks = blockIdx.x % KS;
     const int64_t m0 = grp * 16;
     const int64_t T = K / 32, s0 = ks * T / KS, s1 = (ks + 1) * T / KS;
@@ -170,67 +180,127 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
     }
 
     if (KS > 1) {
-        // Partials to this workgroup's slot (16 rpad floats and 16 doubles);
-        // prepass_combine finishes the group.
-        f32x4 *pu = reinterpret_cast<f32x4 *>(a.ws + a.L.preu);
-        double *pz = reinterpret_cast<double *>(a.ws + a.L.prez);
-        const int64_t slot = grp * KS + ks;
-        for (int tile = wave; tile < ntile; tile += PRE_WAVES)
-            pu[(slot * ntile + tile) * 64 + lane] = s_uw[tile][lane];
-        if (tid < 16)
-            pz[slot * 16 + tid] = s_zw[tid];
-        return;
+        // Tagged slice partials: [slot][tile][lane][4] words of u and [slot][token][2]
+        // words of the fp64 logit, slot = group * pre_ks + slice.
+        uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.L.preu);
+        uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.L.prez);
+        if (tid == 0) {
+            s_tag = epoch_tag(claimed + opaque_zero64());
+            s_bad = 0;
+        }
+        __syncthreads();
+        const uint32_t tag = s_tag;
+        const int nel = ntile * 256;                      // u elements of a slot
+        const float *uw = reinterpret_cast<const float *>(s_uw);
+        if (ks < KS - 1) {
+            uint64_t *du = pu + (grp * KS + ks) * nel;
+            for (int e = tid; e < nel; e += 64 * PRE_WAVES)
+                store_tagged(du + e, __float_as_uint(uw[e]), tag);
+            if (tid < 16) {
+                const uint64_t zb = __builtin_bit_cast(uint64_t, s_zw[tid]);
+                store_tagged(pz + ((grp * KS + ks) * 16 + tid) * 2, (uint32_t)zb, tag);
+                store_tagged(pz + ((grp * KS + ks) * 16 + tid) * 2 + 1, (uint32_t)(zb >> 32), tag);
+            }
+            return;
+        }
+        // The group's last slice: add the other slices' words, in slice order,
+        // then its own partials.
+        float *uwm = reinterpret_cast<float *>(s_uw);
+        bool ok = true;
+        for (int e0 = 0; ok && e0 < nel; e0 += 64 * PRE_WAVES * PRE_FE) {
+            float sum[PRE_FE];
+#pragma unroll
+            for (int f = 0; f < PRE_FE; f++)
+                sum[f] = 0.f;
+            for (int64_t q0 = 0; ok && q0 < KS - 1; q0 += PRE_FQ) {
+                uint64_t w[PRE_FE][PRE_FQ];
+                for (uint32_t it = 0;; it++) {
+                    bool good = true;
+#pragma unroll
+                    for (int f = 0; f < PRE_FE; f++) {
+                        const int e = e0 + tid + 64 * PRE_WAVES * f;
+                        const int ec = e < nel ? e : nel - 1;
+#pragma unroll
+                        for (int q = 0; q < PRE_FQ; q++) {
+                            const int64_t qq = q0 + q < KS - 1 ? q0 + q : KS - 2;
+                            w[f][q] = load_tagged(pu + (grp * KS + qq) * nel + ec);
+                        }
+                    }
+#pragma unroll
+                    for (int f = 0; f < PRE_FE; f++)
+#pragma unroll
+                        for (int q = 0; q < PRE_FQ; q++)
+                            good &= (uint32_t)(w[f][q] >> 32) == tag;
+                    if (__all(good))
+                        break;
+                    if (it >= a.wait_limit) {
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+#pragma unroll
+                for (int f = 0; f < PRE_FE; f++)
+#pragma unroll
+                    for (int q = 0; q < PRE_FQ; q++)
+                        if (q0 + q < KS - 1)
+                            sum[f] += __uint_as_float((uint32_t)w[f][q]);
+            }
+#pragma unroll
+            for (int f = 0; f < PRE_FE; f++) {
+                const int e = e0 + tid + 64 * PRE_WAVES * f;
+                if (e < nel)
+                    uwm[e] = sum[f] + uwm[e];
+            }
+        }
+        if (tid < 16) {
+            // token tid's logit words of every other slice, PRE_FQ slices at a time
+            double z = 0.0;
+            for (int64_t q0 = 0; ok && q0 < KS - 1; q0 += PRE_FQ) {
+                uint64_t w[PRE_FQ][2];
+                for (uint32_t it = 0;; it++) {
+                    bool good = true;
+#pragma unroll
+                    for (int q = 0; q < PRE_FQ; q++) {
+                        const int64_t qq = q0 + q < KS - 1 ? q0 + q : KS - 2;
+                        const uint64_t *src = pz + ((grp * KS + qq) * 16 + tid) * 2;
+                        w[q][0] = load_tagged(src);
+                        w[q][1] = load_tagged(src + 1);
+                    }
+#pragma unroll
+                    for (int q = 0; q < PRE_FQ; q++)
+                        good &= (uint32_t)(w[q][0] >> 32) == tag && (uint32_t)(w[q][1] >> 32) == tag;
+                    if (__all(good))
+                        break;
+                    if (it >= a.wait_limit) {
+                        ok = false;
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(1);
+                }
+#pragma unroll
+                for (int q = 0; q < PRE_FQ; q++)
+                    if (q0 + q < KS - 1)
+                        z += __builtin_bit_cast(double, (uint64_t)(uint32_t)w[q][0] |
+                                                            ((uint64_t)(uint32_t)w[q][1] << 32));
+            }
+            s_zw[tid] = z + s_zw[tid];
+        }
+        if (!ok)
+            atomicOr(&s_bad, 1u);
+        __syncthreads();
+        if (s_bad) {
+            // an expired wait: the group takes no EC term (g = 0, not selected)
+            if (tid == 0)
+                atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+            if (tid < 16)
+                s_zw[tid] = -INFINITY;
+            for (int e = tid; e < nel; e += 64 * PRE_WAVES)
+                uwm[e] = 0.f;
+            __syncthreads();
+        }
     }
     prepass_finish(a, m0, s_uw, s_zw, s_g, s_act, tid, lane, wave, PRE_WAVES);
-}
-
-// Second launch of a split pre-pass: workgroup g sums the pre_ks slots of token
-// group g in slice order and finishes its 16 tokens.  Waves 0 .. CMB_WAVES - 1
-// sum the u tiles, wave CMB_WAVES the logits.
-__global__ __launch_bounds__(64 * (CMB_WAVES + 1)) void prepass_combine(const LinearArgs a)
-{
-    __shared__ f32x4 s_uw[PRE_TILES][64];
-    __shared__ double s_zw[16];
-    __shared__ float s_g[16];
-    __shared__ int s_act[16];
-    pin_args(a);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int64_t KS = a.pre_ks, grp = blockIdx.x;
-    const int ntile = a.rpad / 16;
-    const f32x4 *pu = reinterpret_cast<const f32x4 *>(a.ws + a.L.preu);
-    const double *pz = reinterpret_cast<const double *>(a.ws + a.L.prez);
-    for (int tile = wave; wave < CMB_WAVES && tile < ntile; tile += CMB_WAVES) {
-        f32x4 u = {0.f, 0.f, 0.f, 0.f};
-        for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
-            f32x4 v[CMB_U];
-#pragma unroll
-            for (int i = 0; i < CMB_U; i++)
-                if (q0 + i < KS)
-                    v[i] = pu[((grp * KS + q0 + i) * ntile + tile) * 64 + lane];
-#pragma unroll
-            for (int i = 0; i < CMB_U; i++)
-                if (q0 + i < KS)
-                    u += v[i];
-        }
-        s_uw[tile][lane] = u;
-    }
-    if (wave == CMB_WAVES && lane < 16) {
-        double z = 0.0;
-        for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
-            double v[CMB_U];
-#pragma unroll
-            for (int i = 0; i < CMB_U; i++)
-                if (q0 + i < KS)
-                    v[i] = pz[(grp * KS + q0 + i) * 16 + lane];
-#pragma unroll
-            for (int i = 0; i < CMB_U; i++)
-                if (q0 + i < KS)
-                    z += v[i];
-        }
-        s_zw[lane] = z;
-    }
-    __syncthreads();
-    prepass_finish(a, grp * 16, s_uw, s_zw, s_g, s_act, tid, lane, wave, CMB_WAVES);
 }
 
 // ------------------------------------------------------------------------ GEMM
@@ -656,12 +726,6 @@ hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
     const unsigned groups = (unsigned)((a.M + 15) / 16);
     hipLaunchKernelGGL(prepass_kernel, dim3(groups * (unsigned)a.pre_ks), dim3(64 * PRE_WAVES), 0,
                        s, a);
-    if (a.pre_ks > 1) {
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess)
-            return e;
-        hipLaunchKernelGGL(prepass_combine, dim3(groups), dim3(64 * (CMB_WAVES + 1)), 0, s, a);
-    }
     return hipGetLastError();
 }
 

@@ -286,6 +286,32 @@ def test_forced_wait_timeout_is_reported():
     assert np.array_equal(y, full)
 
 
+def test_prepass_wait_timeout_drops_group_ec():
+    """The split pre-pass's finisher waits, bounded, for the other slices' tagged
+    words.  With a wait limit of one poll a group may give up: its tokens then
+    take no EC term (each output row is the plain or the compensated row), the
+    expiry is counted, and the next call with the default limit is exact."""
+    d = random_case(32, 512, 4096, 32, oracle.CODES_U4, 0, seed=19)
+    w = gpu_weights(d)
+    ws = sp.new_workspace(32, 512, 4096, 32)
+    plain, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ec=False)
+    full, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
+    assert_close(full, run_oracle(d), "split pre-pass")
+    assert sp.spear_workspace_timeouts(ws) == 0
+    try:
+        sp.spear_set_wait_limit(1)
+        y, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
+        n = sp.spear_workspace_timeouts(ws)
+    finally:
+        sp.spear_set_wait_limit(0)
+    for m in range(d["M"]):
+        assert (np.allclose(y[m], plain[m], rtol=0, atol=1e-5) or
+                np.allclose(y[m], full[m], rtol=0, atol=1e-5)), m
+    print(f"[timeout] expired pre-pass waits: {n}")
+    y, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
+    assert np.array_equal(y, full)
+
+
 @pytest.mark.parametrize("M", [1, 16, 128, 2048])
 def test_c5_stack_layers_sampled(M):
     ec_layer = gen.c5_ec_layers()[0]
