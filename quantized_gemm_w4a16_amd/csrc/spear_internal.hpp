@@ -144,7 +144,7 @@ constexpr int DEC_LDS_MAX = 81920;  // LDS bytes of staged activations (M + 1 ro
 constexpr int EPOCH_CTRS = 64;
 constexpr int EPOCH_STRIDE = 128;
 
-constexpr int PROD_BYTES = 16384; // bytes of A an EC producer workgroup reads, about
+constexpr int PROD_BYTES = 8192;  // bytes of A an EC producer workgroup reads, about
 constexpr int MAX_PROD = 32;      // at most this many EC producer workgroups
 constexpr int PROD_CHUNK = 4;     // producer partials a consumer wave loads per batch
 constexpr int PRE_SLOTS = 512;    // EC pre-pass: (token group, K slice) partial slots, at most
