@@ -490,6 +490,11 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         bid -= a.nprod;
     }
     const bool stream = true;
+    // Stream waves issue ahead of a co-resident producer's waves until their
+    // contraction is done (a producer shares a CU with some stream workgroup,
+    // which otherwise finishes last).
+    if (EC_MODE == 1)
+        __builtin_amdgcn_s_setprio(1);
     const int64_t ksplit = a.ksplit, spw = a.spw;
     const int64_t cg = bid / ksplit, ks = bid - cg * ksplit;
     const int64_t n0 = cg * 16;
@@ -648,6 +653,8 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
             sh.red[wave][lane][i] = acc[i];
         sh.red[wave][lane][4] = rs0[0] + rs1[0];
     }
+    if (EC_MODE == 1)
+        __builtin_amdgcn_s_setprio(0);
     if (EC_MODE == 1 && tid == 0)
         sh.u32[0] = epoch_tag(claimed + opaque_zero64());    // both halves live until here
     __syncthreads();
