@@ -519,9 +519,15 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
 #pragma unroll
                     for (int fn = 0; fn < G2_FN; fn++) {
                         const u32x4 wa = unpack8(wv[fn][d]);
+                        // Two waves a SIMD: the one issuing MFMAs goes first, so
+                        // the other's LDS reads and unpacking fill the gaps.
+                        if (G2_WM == 2)
+                            __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                         for (int fm = 0; fm < G2_FM; fm++)
                             acc[fn][fm] = mfma16(wa, xf[fm], acc[fn][fm]);
+                        if (G2_WM == 2)
+                            __builtin_amdgcn_s_setprio(0);
                     }
                 }
             }
