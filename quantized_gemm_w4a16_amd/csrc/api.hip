@@ -117,12 +117,17 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
         L.pz = off;
         off = align256(off + (size_t)(nprod_max * 16 * 2) * sizeof(uint64_t));
     }
-    L.vhi = L.vlo = L.active = L.preu = L.prez = off;
+    L.vhi = L.vlo = L.vtag = L.active = L.preu = L.prez = off;
     if (r > 0) {
         L.vhi = off;
         off = align256(off + (size_t)(L.mpad * L.rpad) * 2);
         L.vlo = off;
         off = align256(off + (size_t)(L.mpad * L.rpad) * 2);
+        // v as tagged words, when the pre-pass shares the K-split GEMM's launch
+        // (fewer than PRE_GROUPS token groups)
+        L.vtag = off;
+        const int64_t mt = L.mpad < PRE_GROUPS * 16 ? L.mpad : PRE_GROUPS * 16;
+        off = align256(off + (size_t)(mt * L.rpad) * sizeof(uint64_t));
         L.active = off;
         off = align256(off + (size_t)L.mpad * 4);
         // EC pre-pass with K split over workgroups: per-slot partials as tagged
@@ -398,6 +403,24 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
             e = launch_decode(a, ec ? 2 : 0, s);
         break;
     default:
+        if (ec && a.g_ks > 1 && cdiv(M, 16) < PRE_GROUPS) {
+            // K-split GEMM: the pre-pass runs as the first blocks of the GEMM's
+            // launch, on the CUs the GEMM's tiles leave free, and the epilogues
+            // wait for its tagged v.  About that many pre-pass workgroups (at
+            // least 32), each of its waves over at least one step of 32.
+            const int64_t tg = cdiv(M, 16), T = K / 32, pw = a.g_bm == 64 ? 4 : 8;
+            const int64_t gwg = cdiv(N, 256) * cdiv(M, a.g_bm) * a.g_ks;
+            const int64_t room = gwg < 256 - 32 ? 256 - gwg : 32;
+            int64_t ks = cdiv(room, tg);
+            const int64_t most = T / pw > 0 ? T / pw : 1;
+            ks = ks < most ? ks : most;
+            a.pre_ks = ks;
+            a.npre = cdiv(tg * ks, 8) * 8;                // XCD-aligned start of the GEMM blocks
+            e = launch_gemm(a, 2, 0, s);
+            if (e == hipSuccess && (a.idx_out || a.nact_out))
+                e = launch_compact(active, M, a.idx_out, a.nact_out, s);
+            break;
+        }
         if (ec) {
             e = launch_prepass(a, s);
             if (e == hipSuccess && (a.idx_out || a.nact_out))

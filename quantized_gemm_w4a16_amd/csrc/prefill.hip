@@ -17,41 +17,60 @@ namespace {
 // Per token: gate logit in fp64, g, hard-gate flag, u = A x (fp32 via MFMA,
 // natural depth order on both operands), v = g u (0 for skipped tokens) stored
 // as bf16 hi + lo.  Workgroup (group, slice): 16 tokens over one of pre_ks K
-// slices; its PRE_WAVES waves split the slice (wave w takes part
-// (w + block) % PRE_WAVES, so workgroups side by side read different parts of
-// A).  A wave walks its part in chunks of PRE_T 32-deep steps and, per chunk,
-// issues every load (x, up to PRE_RT 16-rank tiles of A, w_g) before it uses
-// any, so one memory round trip covers the chunk.  With one slice the
-// workgroup finishes the tokens itself.  With several, every workgroup but the
-// group's last slice stores its partials as tagged words {value, launch epoch}
-// (relaxed device-coherent stores), and the last slice -- the group's highest
-// block index, dispatched after the others, which never wait -- re-loads the
-// other slices' words until every tag is this launch's (bounded; an expired
-// wait drops the group's EC term and is counted), adds the slices in order
-// and finishes the tokens.  Each word is validated on its own, so no fence or
-// counter is involved (a release fence per workgroup would write back the
-// whole L2).
-constexpr int PRE_WAVES = 8;
+// slices; its PW waves split the slice (wave w takes part (w + block) % PW, so
+// workgroups side by side read different parts of A).  A wave walks its part
+// in chunks of PRE_T 32-deep steps and, per chunk, issues every load (x, up to
+// PRE_RT 16-rank tiles of A, w_g) before it uses any, so one memory round trip
+// covers the chunk.  With one slice the workgroup finishes the tokens itself.
+// With several, every workgroup but the group's last slice stores its partials
+// as tagged words {value, launch epoch} (relaxed device-coherent stores), and
+// the last slice -- the group's highest block index, dispatched after the
+// others, which never wait -- re-loads the other slices' words until every tag
+// is this launch's (bounded; an expired wait drops the group's EC term and is
+// counted), adds the slices in order and finishes the tokens.  Each word is
+// validated on its own, so no fence or counter is involved (a release fence
+// per workgroup would write back the whole L2).
+//
+// The pre-pass runs either as its own launch (8 waves a workgroup; v goes to
+// plain bf16 arrays that the GEMM launch reads) or as the first blocks of the
+// K-split GEMM's launch (the GEMM's 4 or 8 waves a workgroup; v goes out as
+// tagged words {hi | lo << 16, epoch} that the GEMM epilogues wait for).
+constexpr int PRE_WAVES = 8;                   // waves of the stand-alone launch
 constexpr int PRE_T = 8;                       // 32-deep steps per chunk
 constexpr int PRE_RT = 4;                      // 16-rank tiles per pass over the slice
 constexpr int PRE_TILES = SPEAR_MAX_RANK / 16;
 constexpr int PRE_FE = 2;                      // finisher: u elements a thread adds up per batch
-constexpr int PRE_FQ = 16;                     // finisher: slices per batch (loads in flight)
+constexpr int PRE_FQ = 8;                      // finisher: slices per batch (loads in flight)
 constexpr int CMB_U = 16;                      // split-K reduction: slice loads in flight
+
+// The pre-pass's LDS (arrays of PW waves), wherever the launch keeps it.
+template <int PW>
+struct PreShared {
+    f32x4 (*u)[PRE_RT][64];   // [PW]: each wave's u tiles of the current pass
+    double (*z)[64];          // [PW]: each wave's logit partials
+    u32x4 (*wg)[4 * PRE_T];   // [PW]: each wave's w_g of its chunk
+    f32x4 (*uw)[64];          // [PRE_TILES]: the workgroup's u
+    double *zw;               // [16]: the workgroup's logit sums
+    float *g;                 // [16]
+    int *act;                 // [16]
+    uint32_t *tag, *bad;
+};
 
 // The last step of the pre-pass for tokens m0 .. m0 + 15, given their logit
 // sums (without b) in s_zw and u in s_uw (tile t, lane l: ranks 16 t + 4 (l / 16)
 // + i of token l % 16): gate, selection, v = g u as bf16 hi + lo.  Called by
-// every thread of the workgroup; waves below nwaves write v.
+// every thread of the workgroup; waves below nwaves write v (as tagged words
+// when tagged).
 __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_uw)[64],
                                const double *s_zw, float *s_g, int *s_act, int tid, int lane,
-                               int wave, int nwaves)
+                               int wave, int nwaves, bool tagged, uint32_t tag)
 {
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, m = m0 + lr;
     const int rpad = a.rpad;
     uint16_t *vhi = reinterpret_cast<uint16_t *>(a.ws + a.L.vhi);
     uint16_t *vlo = reinterpret_cast<uint16_t *>(a.ws + a.L.vlo);
+    uint64_t *vtag = reinterpret_cast<uint64_t *>(a.ws + a.L.vtag);
     int32_t *active = reinterpret_cast<int32_t *>(a.ws + a.L.active);
     if (tid < 16) {
         const double z = (double)a.b + s_zw[tid];
@@ -77,38 +96,38 @@ __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_
             lo[i] = f2bf(v - bf16f(hi[i]));
         }
         const int64_t off = m * rpad + 16 * tile + 4 * lg;
-        uint2 h, l;
-        h.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
-        h.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
-        l.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
-        l.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
-        *reinterpret_cast<uint2 *>(vhi + off) = h;
-        *reinterpret_cast<uint2 *>(vlo + off) = l;
+        if (tagged) {
+#pragma unroll
+            for (int i = 0; i < 4; i++)
+                store_tagged(vtag + off + i, (uint32_t)hi[i] | ((uint32_t)lo[i] << 16), tag);
+        } else {
+            uint2 h, l;
+            h.x = (uint32_t)hi[0] | ((uint32_t)hi[1] << 16);
+            h.y = (uint32_t)hi[2] | ((uint32_t)hi[3] << 16);
+            l.x = (uint32_t)lo[0] | ((uint32_t)lo[1] << 16);
+            l.y = (uint32_t)lo[2] | ((uint32_t)lo[3] << 16);
+            *reinterpret_cast<uint2 *>(vhi + off) = h;
+            *reinterpret_cast<uint2 *>(vlo + off) = l;
+        }
     }
 }
 
-__global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArgs a)
+// One pre-pass workgroup (block bid of the pre-pass grid, PW waves).  claimed
+// is thread 0's epoch claim; the launch claims in every block when the slices
+// exchange words or v goes out tagged.
+template <int PW>
+__device__ __forceinline__ void prepass_body(const LinearArgs &a, const int64_t bid,
+                                             const PreShared<PW> &sh, const uint64_t claimed,
+                                             const bool tagged)
 {
-    __shared__ f32x4 s_u[PRE_WAVES][PRE_RT][64];
-    __shared__ double s_z[PRE_WAVES][64];
-    __shared__ u32x4 s_wg[PRE_WAVES][4 * PRE_T];   // each wave's w_g for its chunk
-    __shared__ f32x4 s_uw[PRE_TILES][64];          // the workgroup's u
-    __shared__ double s_zw[16];
-    __shared__ float s_g[16];
-    __shared__ int s_act[16];
-    __shared__ uint32_t s_tag, s_bad;
-    pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, K = a.K, KS = a.pre_ks;
-    uint64_t claimed = opaque_zero64();
-    if (KS > 1 && tid == 0)
-        claimed = epoch_claim(a);                         // back long before it is used
-    const int64_t grp = blockIdx.x / KS, ks = blockIdx.x % KS;
+    const int64_t grp = bid / KS, ks = bid % KS;
     const int64_t m0 = grp * 16;
     const int64_t T = K / 32, s0 = ks * T / KS, s1 = (ks + 1) * T / KS;
-    const int64_t part = (wave + blockIdx.x) % PRE_WAVES;
-    const int64_t t0 = s0 + part * (s1 - s0) / PRE_WAVES, t1 = s0 + (part + 1) * (s1 - s0) / PRE_WAVES;
+    const int64_t part = (wave + bid) % PW;
+    const int64_t t0 = s0 + part * (s1 - s0) / PW, t1 = s0 + (part + 1) * (s1 - s0) / PW;
     const int64_t m = m0 + lr;
     const bool mv = m < M;
     const int r = a.r, ntile = a.rpad / 16;
@@ -135,7 +154,7 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
             // lane 4 i + p holds w_g[32 (tc + i) + 8 p .. + 7]
             const u32x4 wq = (q0 == 0 && lane < 4 * n) ? ld16(a.wg + 32 * tc + 8 * lane) : zero4();
             if (q0 == 0 && lane < 4 * PRE_T)
-                s_wg[wave][lane] = wq;
+                sh.wg[wave][lane] = wq;
 #pragma unroll
             for (int i = 0; i < PRE_T; i++) {
                 if (i < n) {
@@ -144,7 +163,7 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
                         if (q0 + q < ntile)
                             acc[q] = mfma16(av[i][q], xf[i], acc[q]);
                     if (q0 == 0) {
-                        const u32x4 w = s_wg[wave][4 * i + lg];
+                        const u32x4 w = sh.wg[wave][4 * i + lg];
 #pragma unroll
                         for (int e = 0; e < 4; e++) {
                             zp += (double)(__uint_as_float(xf[i][e] << 16) *
@@ -158,46 +177,49 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
         }
 #pragma unroll
         for (int q = 0; q < PRE_RT; q++)
-            s_u[wave][q][lane] = acc[q];
+            sh.u[wave][q][lane] = acc[q];
         if (q0 == 0)
-            s_z[wave][lane] = zp;
+            sh.z[wave][lane] = zp;
         __syncthreads();
         // the workgroup's partials: waves in order (then lane groups for z)
         if (wave < PRE_RT && q0 + wave < ntile) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
-            for (int w = 0; w < PRE_WAVES; w++)
-                u += s_u[w][wave][lane];
-            s_uw[q0 + wave][lane] = u;
+            for (int w = 0; w < PW; w++)
+                u += sh.u[w][wave][lane];
+            sh.uw[q0 + wave][lane] = u;
         }
-        if (q0 == 0 && wave == PRE_RT && lane < 16) {
+        if (q0 == 0 && wave == PRE_RT % PW && lane < 16) {
             double z = 0.0;
-            for (int w = 0; w < PRE_WAVES; w++)
+            for (int w = 0; w < PW; w++)
                 for (int q = 0; q < 4; q++)
-                    z += s_z[w][lane + 16 * q];
-            s_zw[lane] = z;
+                    z += sh.z[w][lane + 16 * q];
+            sh.zw[lane] = z;
         }
         __syncthreads();
     }
 
+    uint32_t tag = 0;
+    if (KS > 1 || tagged) {
+        if (tid == 0) {
+            *sh.tag = epoch_tag(claimed + opaque_zero64());
+            *sh.bad = 0;
+        }
+        __syncthreads();
+        tag = *sh.tag;
+    }
     if (KS > 1) {
         // Tagged slice partials: [slot][tile][lane][4] words of u and [slot][token][2]
         // words of the fp64 logit, slot = group * pre_ks + slice.
         uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.L.preu);
         uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.L.prez);
-        if (tid == 0) {
-            s_tag = epoch_tag(claimed + opaque_zero64());
-            s_bad = 0;
-        }
-        __syncthreads();
-        const uint32_t tag = s_tag;
         const int nel = ntile * 256;                      // u elements of a slot
-        const float *uw = reinterpret_cast<const float *>(s_uw);
+        const float *uw = reinterpret_cast<const float *>(sh.uw);
         if (ks < KS - 1) {
             uint64_t *du = pu + (grp * KS + ks) * nel;
-            for (int e = tid; e < nel; e += 64 * PRE_WAVES)
+            for (int e = tid; e < nel; e += 64 * PW)
                 store_tagged(du + e, __float_as_uint(uw[e]), tag);
             if (tid < 16) {
-                const uint64_t zb = __builtin_bit_cast(uint64_t, s_zw[tid]);
+                const uint64_t zb = __builtin_bit_cast(uint64_t, sh.zw[tid]);
                 store_tagged(pz + ((grp * KS + ks) * 16 + tid) * 2, (uint32_t)zb, tag);
                 store_tagged(pz + ((grp * KS + ks) * 16 + tid) * 2 + 1, (uint32_t)(zb >> 32), tag);
             }
@@ -205,9 +227,9 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
         }
         // The group's last slice: add the other slices' words, in slice order,
         // then its own partials.
-        float *uwm = reinterpret_cast<float *>(s_uw);
+        float *uwm = reinterpret_cast<float *>(sh.uw);
         bool ok = true;
-        for (int e0 = 0; ok && e0 < nel; e0 += 64 * PRE_WAVES * PRE_FE) {
+        for (int e0 = 0; ok && e0 < nel; e0 += 64 * PW * PRE_FE) {
             float sum[PRE_FE];
 #pragma unroll
             for (int f = 0; f < PRE_FE; f++)
@@ -218,7 +240,7 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
                     bool good = true;
 #pragma unroll
                     for (int f = 0; f < PRE_FE; f++) {
-                        const int e = e0 + tid + 64 * PRE_WAVES * f;
+                        const int e = e0 + tid + 64 * PW * f;
                         const int ec = e < nel ? e : nel - 1;
 #pragma unroll
                         for (int q = 0; q < PRE_FQ; q++) {
@@ -248,7 +270,7 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
             }
 #pragma unroll
             for (int f = 0; f < PRE_FE; f++) {
-                const int e = e0 + tid + 64 * PRE_WAVES * f;
+                const int e = e0 + tid + 64 * PW * f;
                 if (e < nel)
                     uwm[e] = sum[f] + uwm[e];
             }
@@ -284,23 +306,41 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
                         z += __builtin_bit_cast(double, (uint64_t)(uint32_t)w[q][0] |
                                                             ((uint64_t)(uint32_t)w[q][1] << 32));
             }
-            s_zw[tid] = z + s_zw[tid];
+            sh.zw[tid] = z + sh.zw[tid];
         }
         if (!ok)
-            atomicOr(&s_bad, 1u);
+            atomicOr(sh.bad, 1u);
         __syncthreads();
-        if (s_bad) {
+        if (*sh.bad) {
             // an expired wait: the group takes no EC term (g = 0, not selected)
             if (tid == 0)
                 atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
             if (tid < 16)
-                s_zw[tid] = -INFINITY;
-            for (int e = tid; e < nel; e += 64 * PRE_WAVES)
+                sh.zw[tid] = -INFINITY;
+            for (int e = tid; e < nel; e += 64 * PW)
                 uwm[e] = 0.f;
             __syncthreads();
         }
     }
-    prepass_finish(a, m0, s_uw, s_zw, s_g, s_act, tid, lane, wave, PRE_WAVES);
+    prepass_finish(a, m0, sh.uw, sh.zw, sh.g, sh.act, tid, lane, wave, PW, tagged, tag);
+}
+
+__global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArgs a)
+{
+    __shared__ f32x4 s_u[PRE_WAVES][PRE_RT][64];
+    __shared__ double s_z[PRE_WAVES][64];
+    __shared__ u32x4 s_wg[PRE_WAVES][4 * PRE_T];
+    __shared__ f32x4 s_uw[PRE_TILES][64];
+    __shared__ double s_zw[16];
+    __shared__ float s_g[16];
+    __shared__ int s_act[16];
+    __shared__ uint32_t s_tag, s_bad;
+    pin_args(a);
+    uint64_t claimed = opaque_zero64();
+    if (a.pre_ks > 1 && threadIdx.x == 0)
+        claimed = epoch_claim(a);                         // back long before it is used
+    const PreShared<PRE_WAVES> sh = {s_u, s_z, s_wg, s_uw, s_zw, s_g, s_act, &s_tag, &s_bad};
+    prepass_body<PRE_WAVES>(a, blockIdx.x, sh, claimed, false);
 }
 
 // ------------------------------------------------------------------------ GEMM
@@ -369,9 +409,37 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     uint8_t *const s_xb[G2_STAGES] = {s_x0, s_x1, s_x2};
     uint8_t *const s_wb[G2_STAGES] = {s_w0, s_w1, s_w2};
 
+    __shared__ uint32_t s_tagg, s_tbad;
     pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
+
+    // EC == 2: the launch's first a.npre blocks are the EC pre-pass (its LDS
+    // carved out of the stage buffers); every block claims the launch epoch.
+    uint64_t claimed = opaque_zero64();
+    if (EC == 2) {
+        if (tid == 0)
+            claimed = epoch_claim(a);
+        if ((int64_t)blockIdx.x < a.npre) {
+            constexpr int PW = G2_NT / 64;
+            static_assert(PW * PRE_RT * 64 * 16 <= G2_XB && PRE_TILES * 64 * 16 <= G2_XB &&
+                          PW * 64 * 8 + PW * 4 * PRE_T * 16 <= G2_XB && 16 * 16 + 8 <= G2_WB,
+                          "pre-pass LDS inside the stage buffers");
+            const PreShared<PW> sh = {
+                reinterpret_cast<f32x4(*)[PRE_RT][64]>(s_x0),
+                reinterpret_cast<double(*)[64]>(s_x2),
+                reinterpret_cast<u32x4(*)[4 * PRE_T]>(s_x2 + PW * 64 * 8),
+                reinterpret_cast<f32x4(*)[64]>(s_x1),
+                reinterpret_cast<double *>(s_w0),
+                reinterpret_cast<float *>(s_w0 + 128),
+                reinterpret_cast<int *>(s_w0 + 192),
+                reinterpret_cast<uint32_t *>(s_w0 + 256),
+                reinterpret_cast<uint32_t *>(s_w0 + 260)};
+            if ((int64_t)blockIdx.x < ((a.M + 15) / 16) * a.pre_ks)
+                prepass_body<PW>(a, blockIdx.x, sh, claimed, true);
+            return;
+        }
+    }
     const int lr = lane & 15, lg = lane >> 4;
     const int wn = wave % G2_WN, wm = wave / G2_WN;
     const int64_t M = a.M, N = a.N, K = a.K;
@@ -383,7 +451,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     // Blocks are dealt round-robin to the 8 XCDs; give each XCD a contiguous run
     // of units (channels fastest, then tokens, then K slices) so its L2 shares
     // activation rows.
-    const int64_t bid = blockIdx.x;
+    const int64_t bid = (int64_t)blockIdx.x - (EC == 2 ? a.npre : 0);   // npre % 8 == 0
     const int64_t q8 = nunits / 8, r8 = nunits % 8;
     const int64_t xcd = bid % 8, loc = bid / 8;
     const int64_t unit = xcd * q8 + (xcd < r8 ? xcd : r8) + loc;
@@ -457,10 +525,33 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
             bf[fn] = (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
         }
     };
-    constexpr bool ECPRE = EC && G2_WM == 1;
+    constexpr bool ECPRE = EC == 1 && G2_WM == 1;
     u32x4 pvh[G2_FM], pvl[G2_FM], pbf[G2_FN];
     if (ECPRE && ks < a.rpad / 32)
         ec_load((int)ks, pvh, pvl, pbf);
+    // EC == 2, one wave a SIMD: the B rows of the slice's first rank chunk now
+    // (v comes from this launch's pre-pass blocks, at the end).
+    if (EC == 2 && G2_WM == 1 && ks < a.rpad / 32) {
+        const int j = 32 * (int)ks + 8 * lg;
+#pragma unroll
+        for (int fn = 0; fn < G2_FN; fn++) {
+            const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
+            pbf[fn] = (nn < N && j < a.r) ? ld16(a.B + nn * a.r + j) : zero4();
+        }
+    }
+    // The epilogue's scales and zero-point bytes, loaded now so that their round
+    // trip overlaps the main loop.
+    float sc_raw[G2_FN][4];
+    uint32_t zb_raw[G2_FN][4];
+#pragma unroll
+    for (int fn = 0; fn < G2_FN; fn++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            int64_t nn = n0 + (wn * G2_FN + fn) * 16 + 4 * lg + i;
+            nn = nn < N ? nn : N - 1;
+            sc_raw[fn][i] = a.scales[nn];
+            zb_raw[fn][i] = load_zero_byte(a.zeros, a.scales, nn);
+        }
 
     f32x4 acc[G2_FN][G2_FM], rsq[G2_FM];
     const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
@@ -542,6 +633,10 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
         for (int fm = 0; fm < G2_FM; fm++)
             s_rsp[wn][(wm * G2_FM + fm) * 16 + lr] = rsq[fm][0];
     }
+    if (EC == 2 && tid == 0) {
+        s_tagg = epoch_tag(claimed + opaque_zero64());
+        s_tbad = 0;
+    }
     __syncthreads();
 
     // Epilogue: scale and offset removal, the EC term, store.
@@ -549,10 +644,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     for (int fn = 0; fn < G2_FN; fn++) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            int64_t nn = n0 + (wn * G2_FN + fn) * 16 + 4 * lg + i;
-            nn = nn < N ? nn : N - 1;
-            const float sn = a.scales[nn];
-            const float zc = UNPACK_OFF + zero_point(a.zeros, load_zero_byte(a.zeros, a.scales, nn));
+            const float sn = sc_raw[fn][i];
+            const float zc = UNPACK_OFF + zero_point(a.zeros, zb_raw[fn][i]);
 #pragma unroll
             for (int fm = 0; fm < G2_FM; fm++) {
                 const int row = (wm * G2_FM + fm) * 16 + lr;
@@ -561,7 +654,97 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
             }
         }
     }
-    if (EC && ks < a.rpad / 32) {
+    if (EC == 2 && ks < a.rpad / 32) {
+        // v of the tile's tokens as tagged words from the launch's pre-pass
+        // blocks: word {hi | lo << 16, epoch} per (token, rank).  Each thread
+        // loads its share of the tile's words into LDS (stage buffer 0, free
+        // after the main loop) until every tag is this launch's; when they are
+        // not all there at the first try, a wave polls one word (one request)
+        // before it reloads, so that early tiles do not flood the memory system
+        // the pre-pass needs.  Bounded; an expired wait drops this chunk's EC
+        // term for the whole tile and is counted.
+        const uint64_t *vtag = reinterpret_cast<const uint64_t *>(a.ws + a.L.vtag);
+        const uint32_t tag = s_tagg;
+        const int rpad = a.rpad, r = a.r;
+        uint32_t *s_v = reinterpret_cast<uint32_t *>(s_x0);          // [G2_BM][32] payloads
+        static_assert(G2_BM * 32 * 4 <= G2_XB && (G2_BM * 32) % G2_NT == 0, "v staging");
+        constexpr int VW = G2_BM * 32 / G2_NT;                        // words a thread loads
+        for (int64_t t = ks; t < rpad / 32; t += KS) {
+            const int j = 32 * (int)t + 8 * lg;
+            u32x4 bf[G2_FN];
+#pragma unroll
+            for (int fn = 0; fn < G2_FN; fn++) {
+                const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
+                bf[fn] = (G2_WM == 1 && t == ks) ? pbf[fn]
+                         : (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
+            }
+            bool ok = true;
+            for (uint32_t it = 0;; it++) {
+                bool good = true;
+                uint64_t w[VW];
+#pragma unroll
+                for (int q = 0; q < VW; q++) {
+                    const int e = tid + G2_NT * q;                      // token e / 32, rank e % 32
+                    const int64_t mm = m0 + e / 32 < M ? m0 + e / 32 : M - 1;
+                    w[q] = load_tagged(vtag + mm * rpad + 32 * t + e % 32);
+                }
+#pragma unroll
+                for (int q = 0; q < VW; q++) {
+                    good &= (uint32_t)(w[q] >> 32) == tag;
+                    s_v[tid + G2_NT * q] = (uint32_t)w[q];
+                }
+                if (__all(good))
+                    break;
+                if (it >= a.wait_limit) {
+                    ok = false;
+                    break;
+                }
+                if (it == 0) {
+                    // not there yet: poll one word (one request a wave) until the
+                    // tile's last token has it, rather than reload them all
+                    const int64_t ml = m0 + G2_BM - 1 < M ? m0 + G2_BM - 1 : M - 1;
+                    const uint64_t *probe = vtag + ml * rpad + 32 * t + 31;
+                    for (uint32_t ip = 0; ip < a.wait_limit; ip++) {
+                        if ((uint32_t)(load_tagged(probe) >> 32) == tag)
+                            break;
+                        __builtin_amdgcn_s_sleep(8);
+                    }
+                }
+                __builtin_amdgcn_s_sleep(4);
+            }
+            if (!ok && lane == 0)
+                atomicOr(&s_tbad, 1u << (t & 31));
+            __syncthreads();
+            if (s_tbad & (1u << (t & 31))) {
+                if (tid == 0)
+                    atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+                __syncthreads();                                      // s_v is rewritten next
+                continue;
+            }
+#pragma unroll
+            for (int fm = 0; fm < G2_FM; fm++) {
+                const int row = (wm * G2_FM + fm) * 16 + lr;
+                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(s_v + row * 32 + 8 * lg);
+                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(s_v + row * 32 + 8 * lg + 4);
+                const uint32_t w8[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                const bool mv = m0 + row < M;
+                u32x4 vh, vl;
+#pragma unroll
+                for (int p = 0; p < 4; p++) {
+                    const uint32_t w0 = w8[2 * p], w1 = w8[2 * p + 1];
+                    vh[p] = mv ? (w0 & 0xFFFFu) | (w1 << 16) : 0u;
+                    vl[p] = mv ? (w0 >> 16) | (w1 & 0xFFFF0000u) : 0u;
+                }
+#pragma unroll
+                for (int fn = 0; fn < G2_FN; fn++) {
+                    acc[fn][fm] = mfma16(bf[fn], vh, acc[fn][fm]);
+                    acc[fn][fm] = mfma16(bf[fn], vl, acc[fn][fm]);
+                }
+            }
+            __syncthreads();                                          // s_v is rewritten next
+        }
+    }
+    if (EC == 1 && ks < a.rpad / 32) {
         // Rank chunks of 32: slice ks takes chunks ks, ks + KS, ... (the
         // second launch adds the slices), so a K split also splits the EC.
         const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
@@ -703,8 +886,10 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
     const int64_t bm = 16 * FM * WM;
     const int64_t ntiles = ((a.N + G2_BN - 1) / G2_BN) * ((a.M + bm - 1) / bm);
     const dim3 block(64 * G2_WN * WM);
-    if (a.g_ks > 1) {
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1>), dim3((unsigned)(ntiles * a.g_ks)),
+    if (EC == 2 || a.g_ks > 1) {
+        // EC == 2 (K split only): the pre-pass blocks come first in the grid
+        const int64_t pre = EC == 2 ? a.npre : 0;
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1>), dim3((unsigned)(pre + ntiles * a.g_ks)),
                            block, 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -718,10 +903,12 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
                                dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    if (a.out_f32)
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1>), dim3((unsigned)ntiles), block, 0, s, a);
-    else
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0>), dim3((unsigned)ntiles), block, 0, s, a);
+    if constexpr (EC != 2) {
+        if (a.out_f32)
+            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1>), dim3((unsigned)ntiles), block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0>), dim3((unsigned)ntiles), block, 0, s, a);
+    }
     return hipGetLastError();
 }
 
@@ -738,8 +925,13 @@ hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStream_t s)
 {
     (void)force_large;                                    // a.g_bm and a.g_ks carry the choice
-    if (a.g_bm == 64)
+    if (a.g_bm == 64) {
+        if (ec_on == 2)
+            return launch_gemm2_t<1, 4, 2>(a, s);
         return ec_on ? launch_gemm2_t<1, 4, 1>(a, s) : launch_gemm2_t<1, 4, 0>(a, s);
+    }
+    if (ec_on == 2)
+        return launch_gemm2_t<2, 4, 2>(a, s);
     return ec_on ? launch_gemm2_t<2, 4, 1>(a, s) : launch_gemm2_t<2, 4, 0>(a, s);
 }
 

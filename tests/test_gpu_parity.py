@@ -288,9 +288,12 @@ def test_forced_wait_timeout_is_reported():
 
 def test_prepass_wait_timeout_drops_group_ec():
     """The split pre-pass's finisher waits, bounded, for the other slices' tagged
-    words.  With a wait limit of one poll a group may give up: its tokens then
-    take no EC term (each output row is the plain or the compensated row), the
-    expiry is counted, and the next call with the default limit is exact."""
+    words, and here (a K-split GEMM) the GEMM epilogues wait the same way for
+    the pre-pass blocks' tagged v.  With a wait limit of one poll either may give
+    up: the tokens it covers then take no EC term in the channels it covers
+    (each 256-channel block of an output row is the plain or the compensated
+    one), the expiry is counted, and the next call with the default limit is
+    exact."""
     d = random_case(32, 512, 4096, 32, oracle.CODES_U4, 0, seed=19)
     w = gpu_weights(d)
     ws = sp.new_workspace(32, 512, 4096, 32)
@@ -305,9 +308,11 @@ def test_prepass_wait_timeout_drops_group_ec():
     finally:
         sp.spear_set_wait_limit(0)
     for m in range(d["M"]):
-        assert (np.allclose(y[m], plain[m], rtol=0, atol=1e-5) or
-                np.allclose(y[m], full[m], rtol=0, atol=1e-5)), m
-    print(f"[timeout] expired pre-pass waits: {n}")
+        for c in range(0, d["N"], 256):
+            blk = slice(c, c + 256)
+            assert (np.allclose(y[m, blk], plain[m, blk], rtol=0, atol=1e-5) or
+                    np.allclose(y[m, blk], full[m, blk], rtol=0, atol=1e-5)), (m, c)
+    print(f"[timeout] expired waits: {n}")
     y, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
     assert np.array_equal(y, full)
 
