@@ -80,7 +80,9 @@ typedef int32_t spear_status;
 #define SPEAR_PATH_DECODE        1 /* M <= 16: one launch, EC fused into the epilogue   */
 #define SPEAR_PATH_PREFILL       2 /* any M: EC pre-pass, then the MFMA GEMM whose
                                       epilogue applies the EC; with few output tiles
-                                      K is split and a second launch adds the slices */
+                                      K is split, the pre-pass runs as the first
+                                      blocks of the GEMM's launch, and a second
+                                      launch adds the slices                           */
 #define SPEAR_PATH_DECODE_2PASS  3 /* M <= 16: EC pre-pass, then the decode kernel      */
 #define SPEAR_PATH_PREFILL_LARGE 4 /* any M: EC pre-pass, then the 256 x 128-tile MFMA
                                       GEMM over whole K (the prefill path's choice
@@ -188,9 +190,11 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
                                   void *stream);
 
 /*
- * The fused decode kernel's epilogue waits (bounded) for the EC partials that
- * other workgroups of the same launch produce.  If a wait exceeds the limit
- * the affected outputs are written without the EC and a counter in the
+ * Some launches wait (bounded) for EC values that other workgroups of the same
+ * launch produce: the fused decode kernel's epilogue, the split pre-pass's last
+ * slice and, on the K-split prefill path, the GEMM epilogue.  If a wait exceeds
+ * the limit the outputs it covers (a decode workgroup's channels, a pre-pass
+ * token group, a GEMM tile) are written without the EC and a counter in the
  * workspace is incremented.  spear_set_wait_limit sets the limit in polling
  * rounds for later launches (0 restores the default, about a second);
  * spear_workspace_timeouts synchronises `stream`, copies the counter to
