@@ -14,7 +14,9 @@ points, EC factors and gate weights, activations in, fp32 outputs out), in GB/s.
 The line also carries the plain-W4 time of the same steps (EC overhead), the
 roofline of the decode kernel and the CPU oracle timed on a bounded sample.
 
---workload c4 times the prefill configuration instead (M = N = K = 4096,
+--workload c1 times the small layer (M = 16, K = N = 1024, rank 16; launch
+latency bound, reported in microseconds a call and GB/s); --workload c4 times
+the prefill configuration instead (M = N = K = 4096,
 TFLOP/s); --workload c3 the MLP up-projection at M = 64 (K = 4096, N = 14336,
 rank 64, hard gate); --workload c5 a 28-layer stack of a 1.5B-class decoder's
 seven linears (ECs on 4 layers) at --c5-m tokens, reporting the stack time
@@ -44,7 +46,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="c2", choices=["c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--c5-m", type=int, default=1, choices=[1, 16, 128, 2048],
                    help="tokens per call of the C5 stack")
     p.add_argument("--copies", type=int, default=64)
@@ -270,6 +272,53 @@ def run_c4(args, torch, sp, gen):
     }
 
 
+def run_c1(args, torch, sp, gen):
+    """C1: M = 16, K = N = 1024, symmetric codes with fp32 scales, EC rank 16
+    with the soft gate.  One call moves about 0.6 MB, so it is bound by launch
+    latency; the weights rotate over 512 copies (more than the Infinity Cache)."""
+    d = gen.make(1)
+    M, N, K, r = d["M"], d["N"], d["K"], d["ec"]["r"]
+    R = max(2, min(args.copies * 8, 512))
+    ws, ecs = build_copies(d, R, torch, sp)
+    x = dev(d["x"], torch)
+    y = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    wsp = sp.new_workspace(M, N, K, r)
+
+    def steps_fn(use_ec):
+        def record(n):
+            for i in range(n):
+                sp.spear_w4_linear(x, ws[i % R], ecs[i % R] if use_ec else None, y=y,
+                                   workspace=wsp)
+        return record
+
+    for _ in range(args.warmup):
+        steps_fn(True)(1)
+    torch.cuda.synchronize()
+    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
+    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    assert sp.spear_workspace_timeouts(wsp) == 0
+    w, ecb, io = layer_bytes(M, N, K, r, False)
+    ms = t_ec / args.steps
+    gbs = (w + ecb + io) / (ms * 1e-3) / 1e9
+    return {
+        "metric": METRIC, "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "C1 small layer: M=16, K=N=1024, int4 symmetric per-channel "
+                               "(fp32 scales), bf16 activations N(0,1), EC rank 16 soft gate, "
+                               "fp32 output",
+                   "rotating_weight_copies": R},
+        "us_per_call": round(ms * 1e3, 3),
+        "plain_us_per_call": round(t_plain / args.steps * 1e3, 3),
+        "ec_overhead": round(t_ec / t_plain - 1.0, 4),
+        "plain_GBps": round((w + io) / (t_plain / args.steps * 1e-3) / 1e9, 2),
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<1,1,2,0> (fused EC, 16 tokens)"},
+    }
+
+
 def run_c3(args, torch, sp, gen):
     """C3: M = 64, K = 4096, N = 14336, EC rank 64 with the hard gate (about 40 %
     of tokens skip).  Near the ridge: GB/s and TFLOP/s both reported."""
@@ -394,7 +443,7 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     sp.load()
-    run = {"c2": run_c2, "c3": run_c3, "c4": run_c4, "c5": run_c5}[args.workload]
+    run = {"c1": run_c1, "c2": run_c2, "c3": run_c3, "c4": run_c4, "c5": run_c5}[args.workload]
     out = run(args, torch, sp, gen)
     if args.copy_calibration:
         out["copy_calibration_bytes"] = copy_calibration(torch)

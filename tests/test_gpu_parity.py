@@ -244,17 +244,20 @@ def test_rows_independent_of_batch():
 
 
 def test_workspace_reuse_across_calls():
-    """One workspace serves a sequence of fused decode calls of different shapes:
-    each call advances every one of the 64 launch counters after the 256-byte
-    header (64-bit, 128 bytes apart) by exactly 2^32, whatever its grid, and
-    leaves the header words zero."""
-    ws = sp.new_workspace(16, 1024, 4096, 64)
-    shapes = [(1, 1024, 4096, 64), (16, 512, 2048, 32), (4, 1024, 4096, 64), (1, 1024, 4096, 64)]
-    for (M, N, K, r) in shapes:
+    """One workspace serves a sequence of calls of different shapes that each
+    make one launch with a launch epoch (the fused decode kernel, or the K-split
+    GEMM with the pre-pass in its first blocks): each call advances every one of
+    the 64 launch counters after the 256-byte header (64-bit, 128 bytes apart)
+    by exactly 2^32, whatever its grid, and leaves the header words zero."""
+    ws = sp.new_workspace(64, 1024, 4096, 64)
+    shapes = [(1, 1024, 4096, 64, sp.PATH_DECODE), (64, 1024, 4096, 64, sp.PATH_PREFILL),
+              (16, 512, 2048, 32, sp.PATH_DECODE), (40, 1024, 4096, 64, sp.PATH_PREFILL),
+              (4, 1024, 4096, 64, sp.PATH_DECODE), (1, 1024, 4096, 64, sp.PATH_DECODE)]
+    for (M, N, K, r, path) in shapes:
         d = random_case(M, N, K, r, oracle.CODES_U4, 1, seed=M + N + K)
         assert ws.numel() >= sp.spear_w4_linear_workspace_size(M, N, K, r)
-        y, _ = run_gpu(d, path=sp.PATH_DECODE, ws=ws)
-        assert_close(y, run_oracle(d), f"ws reuse {M}x{N}x{K}")
+        y, _ = run_gpu(d, path=path, ws=ws)
+        assert_close(y, run_oracle(d), f"ws reuse {M}x{N}x{K} path={path}")
     head = host(ws[:256 + 64 * 128])
     assert np.all(head[:256] == 0)
     ctr = head[256:].view(np.uint64)[::16]
