@@ -506,8 +506,9 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     };
 
     // EC operands of one 32-rank chunk t: v (hi, lo) of this wave's tokens and
-    // B rows of its channels.  With one wave per SIMD there is room to load the
-    // slice's first chunk now, so its round trip overlaps the main loop.
+    // B rows of its channels.  The slice's first chunk is loaded now, so its
+    // round trip overlaps the main loop (48 registers, which both tile shapes
+    // have to spare).
     auto ec_load = [&](int t, u32x4 *vh, u32x4 *vl, u32x4 *bf) {
         const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
         const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
             bf[fn] = (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
         }
     };
-    constexpr bool ECPRE = EC == 1 && G2_WM == 1;
+    constexpr bool ECPRE = EC == 1;
     u32x4 pvh[G2_FM], pvl[G2_FM], pbf[G2_FN];
     if (ECPRE && ks < a.rpad / 32)
         ec_load((int)ks, pvh, pvl, pbf);
