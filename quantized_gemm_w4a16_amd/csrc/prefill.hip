@@ -112,6 +112,10 @@ __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_
     }
 }
 
+template <int PW>
+__device__ __forceinline__ void prepass_tail(const LinearArgs &a, int64_t grp, int64_t ks,
+                                             const PreShared<PW> &sh, uint64_t claimed, bool tagged);
+
 // One pre-pass workgroup (block bid of the pre-pass grid, PW waves).  claimed
 // is thread 0's epoch claim; the launch claims in every block when the slices
 // exchange words or v goes out tagged.
@@ -197,7 +201,20 @@ __device__ __forceinline__ void prepass_body(const LinearArgs &a, const int64_t 
         }
         __syncthreads();
     }
+    prepass_tail<PW>(a, grp, ks, sh, claimed, tagged);
+}
 
+// The rest of a pre-pass workgroup once sh.uw and sh.zw hold its partials:
+// with K split, the exchange of the slices' tagged partials (the group's last
+// slice adds them); then gate, selection and v.
+template <int PW>
+__device__ __forceinline__ void prepass_tail(const LinearArgs &a, const int64_t grp, const int64_t ks,
+                                             const PreShared<PW> &sh, const uint64_t claimed,
+                                             const bool tagged)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int64_t KS = a.pre_ks, m0 = grp * 16;
+    const int ntile = a.rpad / 16;
     uint32_t tag = 0;
     if (KS > 1 || tagged) {
         if (tid == 0) {
@@ -341,6 +358,173 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
         claimed = epoch_claim(a);                         // back long before it is used
     const PreShared<PRE_WAVES> sh = {s_u, s_z, s_wg, s_uw, s_zw, s_g, s_act, &s_tag, &s_bad};
     prepass_body<PRE_WAVES>(a, blockIdx.x, sh, claimed, false);
+}
+
+// The same pre-pass for ranks up to 64 with its operands staged through LDS.
+// Loaded straight into MFMA operand registers, every 16-byte load of x or A
+// touches 16 rows (64 bytes of each), which caps what one CU takes in; here
+// the workgroup DMAs whole contiguous rows of a K chunk (512 deep at rank 32,
+// 256 at rank 64) -- 16 token rows of x, then rpad rows of A (zero rows past
+// r) -- into a ring of three stage buffers (global_load_lds, 1 KB per
+// instruction, 16-byte row chunks XOR-swizzled by row % 16 so the operand
+// reads below fall in distinct banks), with one barrier per chunk as in the
+// GEMM.  Wave w takes the 32-deep steps w, w + 8, ... of each chunk; its w_g
+// words come by plain loads issued one chunk ahead, just before the next
+// chunk's DMAs, so one vmcnt wait covers both.  (Six stages of 256-deep
+// chunks at rank 32 measured slower: the CU's intake, not the depth in
+// flight, is the limit.)  The sums, the exchange of K slices and the finish
+// are those of prepass_body.
+template <int RPAD>
+__global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
+{
+    constexpr int CK = RPAD == 32 ? 512 : 256;           // depth of a chunk
+    constexpr int SPW = CK / 256;                        // steps of a chunk a wave takes
+    constexpr int RB = CK * 2;                           // bytes of a staged row
+    constexpr int SB = (16 + RPAD) * RB;                 // bytes of a stage
+    constexpr int NI = SB / (8 * 1024);                  // DMAs a wave issues per stage
+    constexpr int NT = RPAD / 16;                        // rank tiles
+    constexpr int RING = 3;
+    constexpr int WAIT = (RING - 2) * NI + (RING - 3) * SPW;   // loads younger than a chunk's
+    static_assert(NI * 8 * 1024 == SB && NT <= PRE_TILES && WAIT < 64, "chunk geometry");
+    static_assert(8 * NT * 64 * 16 <= SB && PRE_TILES * 64 * 16 <= SB, "sums inside the ring");
+    __shared__ __attribute__((aligned(16))) uint8_t s_r0[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_r1[SB];
+    __shared__ __attribute__((aligned(16))) uint8_t s_r2[SB];
+    __shared__ double s_z[8][64];
+    __shared__ double s_zw[16];
+    __shared__ float s_g[16];
+    __shared__ int s_act[16];
+    __shared__ uint32_t s_tag, s_bad;
+    uint8_t *const ring[RING] = {s_r0, s_r1, s_r2};
+    pin_args(a);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int64_t M = a.M, K = a.K, KS = a.pre_ks, r = a.r;
+    uint64_t claimed = opaque_zero64();
+    if (KS > 1 && tid == 0)
+        claimed = epoch_claim(a);
+    const int64_t grp = blockIdx.x / KS, ks = blockIdx.x % KS;
+    const int64_t m0 = grp * 16;
+    const int64_t T = K / 32;
+    const int64_t kb = 32 * (ks * T / KS), ke = 32 * ((ks + 1) * T / KS);   // this slice's depths
+    const int64_t nch = (ke - kb + CK - 1) / CK;
+    const uint8_t *zsrc = a.ws + a.L.zeros + 16 * (lane & 15);
+
+    // DMA instruction i of this wave fills stage bytes (8 i + wave) KB + 16 lane:
+    // row rho, swizzled position p, logical 16-byte chunk c of the row.
+    const uint8_t *src[NI];
+    int coff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; i++) {
+        const int b = (8 * i + wave) * 1024 + 16 * lane;
+        const int rho = b / RB, p = (b % RB) / 16;
+        const int c = (p & ~15) | ((p & 15) ^ (rho & 15));
+        coff[i] = 8 * c;
+        if (rho < 16) {
+            const int64_t m = m0 + rho < M ? m0 + rho : M - 1;
+            src[i] = reinterpret_cast<const uint8_t *>(a.x + m * K + 8 * c);
+        } else {
+            const int64_t j = rho - 16;
+            src[i] = j < r ? reinterpret_cast<const uint8_t *>(a.A + j * K + 8 * c) : nullptr;
+        }
+    }
+    const int64_t clast = nch - 1;
+    auto issue = [&](int64_t ci, uint8_t *buf) {
+        const int64_t k0 = kb + (ci < clast ? ci : clast) * CK;
+#pragma unroll
+        for (int i = 0; i < NI; i++) {
+            const bool v = src[i] != nullptr && k0 + coff[i] < ke;
+            const void *g = v ? (const void *)(src[i] + 2 * k0) : (const void *)zsrc;
+            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)g,
+                                             (__attribute__((address_space(3))) void *)(buf + (8 * i + wave) * 1024),
+                                             16, 0, 0);
+        }
+    };
+    auto issue_wg = [&](int64_t ci, u32x4 *w) {
+#pragma unroll
+        for (int q = 0; q < SPW; q++) {
+            const int64_t k = kb + (ci < clast ? ci : clast) * CK + 32 * (wave + 8 * q) + 8 * lg;
+            w[q] = k < ke ? ld16(a.wg + k) : zero4();
+        }
+    };
+    // operand offsets inside a stage: row lr of x, rows 16 + 16 t + lr of A, all
+    // at logical chunk 4 st + lg of step st (row % 16 == lr for every one of them)
+    int cs[SPW];
+#pragma unroll
+    for (int q = 0; q < SPW; q++) {
+        const int cc = 4 * (wave + 8 * q) + lg;
+        cs[q] = ((cc & ~15) | ((cc & 15) ^ lr)) << 4;
+    }
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    double zp = 0.0;
+    u32x4 wgr[RING][SPW];
+#pragma unroll
+    for (int q = 0; q < RING - 2; q++) {
+        issue(q, ring[q]);
+        issue_wg(q, wgr[q]);
+    }
+    issue(RING - 2, ring[RING - 2]);
+    for (int64_t c0 = 0; c0 < nch; c0 += RING) {
+#pragma unroll
+        for (int j = 0; j < RING; j++) {
+            const int64_t ci = c0 + j;
+            wait_vmcnt<WAIT>();                           // this wave's DMAs of chunk ci and its w_g
+            bare_barrier();                               // every wave's part; chunk ci - 1 free
+            issue_wg(ci + RING - 2, wgr[(j + RING - 2) % RING]);
+            issue(ci + RING - 1, ring[(j + RING - 1) % RING]);
+            if (ci < nch) {
+                const uint8_t *buf = ring[j];
+#pragma unroll
+                for (int q = 0; q < SPW; q++) {
+                    const u32x4 xf = *reinterpret_cast<const u32x4 *>(buf + lr * RB + cs[q]);
+#pragma unroll
+                    for (int t = 0; t < NT; t++) {
+                        const u32x4 av = *reinterpret_cast<const u32x4 *>(buf + (16 + 16 * t + lr) * RB + cs[q]);
+                        acc[t] = mfma16(av, xf, acc[t]);
+                    }
+                    const u32x4 w = wgr[j][q];
+#pragma unroll
+                    for (int e = 0; e < 4; e++) {
+                        zp += (double)(__uint_as_float(xf[e] << 16) * __uint_as_float(w[e] << 16));
+                        zp += (double)(__uint_as_float(xf[e] & 0xFFFF0000u) *
+                                       __uint_as_float(w[e] & 0xFFFF0000u));
+                    }
+                }
+            }
+        }
+    }
+    wait_vmcnt<0>();                                      // the clamped tail loads
+    __syncthreads();                                      // the ring is free
+
+    // the workgroup's partials: waves in order (then lane groups for z)
+    f32x4 (*su)[NT][64] = reinterpret_cast<f32x4(*)[NT][64]>(s_r0);
+    const PreShared<8> sh = {nullptr, s_z, nullptr, reinterpret_cast<f32x4(*)[64]>(s_r1), s_zw, s_g,
+                             s_act, &s_tag, &s_bad};
+#pragma unroll
+    for (int t = 0; t < NT; t++)
+        su[wave][t][lane] = acc[t];
+    s_z[wave][lane] = zp;
+    __syncthreads();
+    if (wave < NT) {
+        f32x4 u = {0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < 8; w++)
+            u += su[w][wave][lane];
+        sh.uw[wave][lane] = u;
+    }
+    if (wave == 4 && lane < 16) {
+        double z = 0.0;
+        for (int w = 0; w < 8; w++)
+            for (int q = 0; q < 4; q++)
+                z += s_z[w][lane + 16 * q];
+        s_zw[lane] = z;
+    }
+    __syncthreads();
+    prepass_tail<8>(a, grp, ks, sh, claimed, false);
 }
 
 // ------------------------------------------------------------------------ GEMM
@@ -917,9 +1101,13 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
 
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 {
-    const unsigned groups = (unsigned)((a.M + 15) / 16);
-    hipLaunchKernelGGL(prepass_kernel, dim3(groups * (unsigned)a.pre_ks), dim3(64 * PRE_WAVES), 0,
-                       s, a);
+    const unsigned grid = (unsigned)((a.M + 15) / 16) * (unsigned)a.pre_ks;
+    if (a.rpad == 32)
+        hipLaunchKernelGGL(prepass2_kernel<32>, dim3(grid), dim3(512), 0, s, a);
+    else if (a.rpad == 64)
+        hipLaunchKernelGGL(prepass2_kernel<64>, dim3(grid), dim3(512), 0, s, a);
+    else
+        hipLaunchKernelGGL(prepass_kernel, dim3(grid), dim3(64 * PRE_WAVES), 0, s, a);
     return hipGetLastError();
 }
 
