@@ -195,7 +195,10 @@ RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 25
           (257, 300, 2080, 24), (200, 300, 352, 32), (129, 513, 192, 16),
           # K split over workgroups with a K tail and EC rank chunks spread over
           # the slices, on both sides of the 64-token tile switch
-          (64, 260, 1184, 96), (65, 700, 1280, 48)]
+          (64, 260, 1184, 96), (65, 700, 1280, 48),
+          # rank 32 with at least 128 token groups: 64-token pre-pass blocks over
+          # K slices, a partial last block and a ragged last slice
+          (2100, 96, 1056, 24)]
 
 
 @pytest.mark.parametrize("M,N,K,r", RAGGED)
