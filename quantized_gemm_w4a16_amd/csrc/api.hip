@@ -21,10 +21,19 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // PROD_BYTES of A times ceil(M / 2).  A workgroup with more tokens streams
 // longer (its activations take more LDS traffic), so its producers may read
 // more each; fewer producers keep the partials every epilogue loads
-// (producers x tokens x ranks) small.
+// (producers x tokens x ranks) small.  Above 8 tokens the producers' own loads
+// are the longest path, so each reads at most 2 PROD_BYTES of A, as long as
+// the partials an epilogue loads stay within PROD_WORDS words.
 static int64_t ec_producers(int64_t mr, int64_t K, int64_t rpad, int64_t *prod_k)
 {
-    int64_t nprod = cdiv(K * rpad * 2, PROD_BYTES * cdiv(mr, 2));
+    const int64_t per = mr > 8 ? 2 : cdiv(mr, 2);
+    int64_t nprod = cdiv(K * rpad * 2, PROD_BYTES * per);
+    if (mr > 8) {
+        const int64_t cap = PROD_WORDS / (mr * rpad);
+        const int64_t base = cdiv(K * rpad * 2, PROD_BYTES * cdiv(mr, 2));
+        const int64_t lim = cap > base ? cap : base;       // never fewer than before
+        nprod = nprod > lim ? lim : nprod;
+    }
     nprod = nprod < 1 ? 1 : (nprod > MAX_PROD ? MAX_PROD : nprod);
     const int64_t most = cdiv(K, DEC_WAVES * 32);           // slices at least 32 deep
     nprod = nprod > most ? most : nprod;

@@ -146,6 +146,7 @@ constexpr int EPOCH_STRIDE = 128;
 
 constexpr int PROD_BYTES = 8192;  // bytes of A an EC producer workgroup reads, about
 constexpr int MAX_PROD = 32;      // at most this many EC producer workgroups
+constexpr int PROD_WORDS = 4096;  // above 8 tokens: partial words an epilogue loads, at most
 constexpr int PROD_CHUNK = 4;     // producer partials a consumer wave loads per batch
 constexpr int PRE_SLOTS = 512;    // EC pre-pass: (token group, K slice) partial slots, at most
                                   // (fewer than PRE_GROUPS groups, about 256 workgroups)
