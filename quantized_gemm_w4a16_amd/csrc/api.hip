@@ -112,11 +112,11 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
     off = align256(off + (size_t)EPOCH_CTRS * EPOCH_STRIDE);
     L.zeros = off;                                        // 256 bytes that stay zero: DMA source
     off = align256(off + 256);
-    L.colcnt = off;
-    off = align256(off + (size_t)L.ncg * sizeof(uint32_t));
+    // Decode with K split over workgroups: tagged 64-bit words {value, launch
+    // epoch} of each range's sums, [channel group][range][lane][5].
     L.splitp = off;
     if (L.ksplit > 1)                                     // any M: a larger M never needs less
-        off = align256(off + (size_t)(L.ncg * L.ksplit * 64 * 5) * sizeof(float));
+        off = align256(off + (size_t)(L.ncg * L.ksplit * 64 * 5) * sizeof(uint64_t));
     // Producer partials, tagged 64-bit words {value, launch epoch}: u per
     // (producer, token slot, rank) and the fp64 gate logit as two words.
     L.pu = off;

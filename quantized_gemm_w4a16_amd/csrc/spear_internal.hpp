@@ -111,24 +111,6 @@ __device__ __forceinline__ float zero_point(const uint8_t *zeros, uint32_t raw)
     return zeros ? (float)raw : 8.f;
 }
 
-// Agent-scope atomics on workspace counters.
-__device__ __forceinline__ uint32_t atomic_add_acqrel(uint32_t *p, uint32_t v)
-{
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t atomic_load_acquire(uint32_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_store_release(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_store_relaxed(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ------------------------------------------------------------ workspace layout
 // Header: 64 uint32 counters, all zero between calls.
 enum {
@@ -153,7 +135,7 @@ constexpr int PRE_SLOTS = 512;    // EC pre-pass: (token group, K slice) partial
 constexpr int PRE_GROUPS = 128;   // EC pre-pass: token groups below which K is split
 
 struct WsLayout {
-    size_t hdr, epoch, zeros, colcnt, splitp, pu, pz, vhi, vlo, vtag, active, preu, prez, gpart, total;
+    size_t hdr, epoch, zeros, splitp, pu, pz, vhi, vlo, vtag, active, preu, prez, gpart, total;
     int64_t ncg, ksplit, spw, nprod, prod_k, rpad, mpad;
 };
 
@@ -219,7 +201,7 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
     pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
     pin_arg(a.pre_ks); pin_arg(a.g_ks); pin_arg(a.npre); pin_arg(a.L.vtag); pin_arg(a.L.gpart); pin_arg(a.L.preu); pin_arg(a.L.prez);
-    pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.colcnt); pin_arg(a.L.splitp); pin_arg(a.L.pu);
+    pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.splitp); pin_arg(a.L.pu);
     pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);
 }

@@ -198,7 +198,10 @@ RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 25
           (64, 260, 1184, 96), (65, 700, 1280, 48),
           # rank 32 with at least 128 token groups: 64-token pre-pass blocks over
           # K slices, a partial last block and a ragged last slice
-          (2100, 96, 1056, 24)]
+          (2100, 96, 1056, 24),
+          # decode with K split over workgroups (16 tokens do not fit one
+          # workgroup's LDS at this depth): three ranges, a ragged last one
+          (12, 1000, 5024, 40)]
 
 
 @pytest.mark.parametrize("M,N,K,r", RAGGED)
@@ -289,6 +292,29 @@ def test_forced_wait_timeout_is_reported():
     print(f"[timeout] expired waits: {n}")
     assert n >= 0
     y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
+    assert np.array_equal(y, full)
+
+
+def test_decode_ksplit_wait_timeout_is_reported():
+    """Decode with K split over workgroups: the channel group's last range waits,
+    bounded, for the other ranges' tagged sums.  With a wait limit of one poll it
+    may give up (the expiry is counted; the missing ranges are left out of those
+    channels); with the default limit the next call is exact."""
+    d = random_case(16, 512, 8192, 32, oracle.CODES_U4, 0, seed=23)
+    w = gpu_weights(d)
+    ws = sp.new_workspace(16, 512, 8192, 32)
+    full, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws, ec=False)
+    assert_close(full, run_oracle(d, ec=None), "decode K split")
+    assert sp.spear_workspace_timeouts(ws) == 0
+    try:
+        sp.spear_set_wait_limit(1)
+        y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws, ec=False)
+        n = sp.spear_workspace_timeouts(ws)
+    finally:
+        sp.spear_set_wait_limit(0)
+    print(f"[timeout] expired K-range waits: {n}")
+    assert n > 0 or np.array_equal(y, full)
+    y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws, ec=False)
     assert np.array_equal(y, full)
 
 
