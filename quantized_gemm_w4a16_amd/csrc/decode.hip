@@ -21,13 +21,13 @@
 //    GEMV (bf16 dot2 into fp32, four accumulators) and a VALU activation sum.
 //    The packed word order makes the unpacked pairs line up with the
 //    activations' own pairs, so the activations are used as loaded.
-//  * When K is split over workgroups, the last one of a channel group (atomic
-//    counter) sums the partial tiles in slice order (deterministic).
+//  * When K is split over workgroups, every range but the last stores its
+//    sums as tagged words (below) and the channel group's last range -- its
+//    highest block index -- adds them in range order (deterministic).
 //  * EC (fused mode): the lowest block indices, which the dispatcher places
-//    first, are `nprod` producer workgroups.  Each reads about 16 KB of A per
-//    pair of tokens (so a producer's share of the memory system is no larger
-//    than a stream workgroup's and its result is ready before the stream
-//    ends), computes the gate-logit partial (fp64) and A.x (MFMA; dot2 for one
+//    first, are `nprod` producer workgroups.  Each reads about 8 KB of A per
+//    pair of tokens, at most 16 KB above 8 tokens (so a producer's share of
+//    the memory system is no larger than a stream workgroup's), computes the gate-logit partial (fp64) and A.x (MFMA; dot2 for one
 //    token) of every token over its K slice, reduces its 4 waves in LDS and
 //    stores the partials as 64-bit words {value, launch epoch}, one relaxed
 //    device-coherent store each, then leaves.  The epilogue of each channel
