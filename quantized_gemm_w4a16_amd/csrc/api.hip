@@ -417,7 +417,7 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
             // launch, on the CUs the GEMM's tiles leave free, and the epilogues
             // wait for its tagged v.  About that many pre-pass workgroups (at
             // least 32), each of its waves over at least one step of 32.
-            const int64_t tg = cdiv(M, 16), T = K / 32, pw = a.g_bm == 64 ? 4 : 8;
+            const int64_t tg = cdiv(M, 16), T = K / 32, pw = 8;   // the GEMM's 8 waves
             const int64_t gwg = cdiv(N, 256) * cdiv(M, a.g_bm) * a.g_ks;
             const int64_t room = gwg < 256 - 32 ? 256 - gwg : 32;
             int64_t ks = cdiv(room, tg);

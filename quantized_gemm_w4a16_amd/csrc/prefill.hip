@@ -46,7 +46,8 @@ constexpr int CMB_U = 16;                      // split-K reduction: slice loads
 // The pre-pass's LDS (arrays of PW waves), wherever the launch keeps it.
 template <int PW>
 struct PreShared {
-    f32x4 (*u)[PRE_RT][64];   // [PW]: each wave's u tiles of the current pass
+    f32x4 (*u)[PRE_RT][64];   // [PW / 2 or PW]: each wave's u tiles of the current pass ...
+    f32x4 (*u_hi)[PRE_RT][64];  // ... and those of waves PW / 2 and up (may follow u)
     double (*z)[64];          // [PW]: each wave's logit partials
     u32x4 (*wg)[4 * PRE_T];   // [PW]: each wave's w_g of its chunk
     f32x4 (*uw)[64];          // [PRE_TILES]: the workgroup's u
@@ -181,7 +182,7 @@ __device__ __forceinline__ void prepass_body(const LinearArgs &a, const int64_t 
         }
 #pragma unroll
         for (int q = 0; q < PRE_RT; q++)
-            sh.u[wave][q][lane] = acc[q];
+            (wave < PW / 2 ? sh.u[wave] : sh.u_hi[wave - PW / 2])[q][lane] = acc[q];
         if (q0 == 0)
             sh.z[wave][lane] = zp;
         __syncthreads();
@@ -189,7 +190,7 @@ __device__ __forceinline__ void prepass_body(const LinearArgs &a, const int64_t 
         if (wave < PRE_RT && q0 + wave < ntile) {
             f32x4 u = {0.f, 0.f, 0.f, 0.f};
             for (int w = 0; w < PW; w++)
-                u += sh.u[w][wave][lane];
+                u += (w < PW / 2 ? sh.u[w] : sh.u_hi[w - PW / 2])[wave][lane];
             sh.uw[q0 + wave][lane] = u;
         }
         if (q0 == 0 && wave == PRE_RT % PW && lane < 16) {
@@ -356,7 +357,7 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
     uint64_t claimed = opaque_zero64();
     if (a.pre_ks > 1 && threadIdx.x == 0)
         claimed = epoch_claim(a);                         // back long before it is used
-    const PreShared<PRE_WAVES> sh = {s_u, s_z, s_wg, s_uw, s_zw, s_g, s_act, &s_tag, &s_bad};
+    const PreShared<PRE_WAVES> sh = {s_u, s_u + PRE_WAVES / 2, s_z, s_wg, s_uw, s_zw, s_g, s_act, &s_tag, &s_bad};
     prepass_body<PRE_WAVES>(a, blockIdx.x, sh, claimed, false);
 }
 
@@ -503,7 +504,7 @@ __global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
 
     // the workgroup's partials: waves in order (then lane groups for z)
     f32x4 (*su)[NT][64] = reinterpret_cast<f32x4(*)[NT][64]>(s_r0);
-    const PreShared<8> sh = {nullptr, s_z, nullptr, reinterpret_cast<f32x4(*)[64]>(s_r1), s_zw, s_g,
+    const PreShared<8> sh = {nullptr, nullptr, s_z, nullptr, reinterpret_cast<f32x4(*)[64]>(s_r1), s_zw, s_g,
                              s_act, &s_tag, &s_bad};
 #pragma unroll
     for (int t = 0; t < NT; t++)
@@ -572,10 +573,15 @@ __device__ __forceinline__ void lds_read4(const uint8_t *base, uint32_t a0, uint
     r3 = *reinterpret_cast<const u32x4 *>(base + a3);
 }
 
-template <int G2_WM, int G2_FM, int SPLIT, int EC, int OUT_F32>
-__global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearArgs a)
+template <int G2_WM, int G2_FM, int SPLIT, int EC, int OUT_F32, int G2_WK = 1>
+__global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const LinearArgs a)
 {
-    constexpr int G2_NT = 64 * G2_WN * G2_WM;             // 256 or 512 threads
+    // G2_WK = 2 (one token row of waves): two waves share each wave column, the
+    // first taking depth steps 0 and 1 of every 128-deep stage, the second 2
+    // and 3, so each SIMD holds two waves; the second adds its sums into the
+    // first's after the main loop.
+    static_assert(G2_WK == 1 || (G2_WK == 2 && G2_WM == 1), "depth split: 64-token tiles");
+    constexpr int G2_NT = 64 * G2_WN * G2_WM * G2_WK;     // 256 or 512 threads
     constexpr int G2_BM = 16 * G2_FM * G2_WM;             // tokens
     constexpr int G2_XB = G2_BM * 256;                    // activation bytes of one stage
     constexpr int G2_XI = G2_XB / (G2_NT * 16);           // activation DMAs a lane, per stage
@@ -601,31 +607,34 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     // EC == 2: the launch's first a.npre blocks are the EC pre-pass (its LDS
     // carved out of the stage buffers); every block claims the launch epoch.
     uint64_t claimed = opaque_zero64();
-    if (EC == 2) {
+    if constexpr (EC == 2) {
         if (tid == 0)
             claimed = epoch_claim(a);
         if ((int64_t)blockIdx.x < a.npre) {
+            // u: waves 0 .. PW/2 - 1 in s_x0, the others in s_x1; the workgroup's u in
+            // s_x2; logit partials and w_g in s_w0; the small arrays in s_w1.
             constexpr int PW = G2_NT / 64;
-            static_assert(PW * PRE_RT * 64 * 16 <= G2_XB && PRE_TILES * 64 * 16 <= G2_XB &&
-                          PW * 64 * 8 + PW * 4 * PRE_T * 16 <= G2_XB && 16 * 16 + 8 <= G2_WB,
+            static_assert((PW / 2) * PRE_RT * 64 * 16 <= G2_XB && PRE_TILES * 64 * 16 <= G2_XB &&
+                          PW * 64 * 8 + PW * 4 * PRE_T * 16 <= G2_WB && 16 * 16 + 8 <= G2_WB,
                           "pre-pass LDS inside the stage buffers");
             const PreShared<PW> sh = {
                 reinterpret_cast<f32x4(*)[PRE_RT][64]>(s_x0),
-                reinterpret_cast<double(*)[64]>(s_x2),
-                reinterpret_cast<u32x4(*)[4 * PRE_T]>(s_x2 + PW * 64 * 8),
-                reinterpret_cast<f32x4(*)[64]>(s_x1),
-                reinterpret_cast<double *>(s_w0),
-                reinterpret_cast<float *>(s_w0 + 128),
-                reinterpret_cast<int *>(s_w0 + 192),
-                reinterpret_cast<uint32_t *>(s_w0 + 256),
-                reinterpret_cast<uint32_t *>(s_w0 + 260)};
+                reinterpret_cast<f32x4(*)[PRE_RT][64]>(s_x1),
+                reinterpret_cast<double(*)[64]>(s_w0),
+                reinterpret_cast<u32x4(*)[4 * PRE_T]>(s_w0 + PW * 64 * 8),
+                reinterpret_cast<f32x4(*)[64]>(s_x2),
+                reinterpret_cast<double *>(s_w1),
+                reinterpret_cast<float *>(s_w1 + 128),
+                reinterpret_cast<int *>(s_w1 + 192),
+                reinterpret_cast<uint32_t *>(s_w1 + 256),
+                reinterpret_cast<uint32_t *>(s_w1 + 260)};
             if ((int64_t)blockIdx.x < ((a.M + 15) / 16) * a.pre_ks)
                 prepass_body<PW>(a, blockIdx.x, sh, claimed, true);
             return;
         }
     }
     const int lr = lane & 15, lg = lane >> 4;
-    const int wn = wave % G2_WN, wm = wave / G2_WN;
+    const int wn = wave % G2_WN, wm = (wave / G2_WN) % G2_WM, wk = wave / (G2_WN * G2_WM);
     const int64_t M = a.M, N = a.N, K = a.K;
     const int64_t tiles_n = (N + G2_BN - 1) / G2_BN, tiles_m = (M + G2_BM - 1) / G2_BM;
     const int64_t ntiles = tiles_n * tiles_m;
@@ -712,7 +721,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     };
     constexpr bool ECPRE = EC == 1;
     u32x4 pvh[G2_FM], pvl[G2_FM], pbf[G2_FN];
-    if (ECPRE && ks < a.rpad / 32)
+    if (ECPRE && wk == 0 && ks < a.rpad / 32)
         ec_load((int)ks, pvh, pvl, pbf);
     // EC == 2, one wave a SIMD: the B rows of the slice's first rank chunk now
     // (v comes from this launch's pre-pass blocks, at the end).
@@ -753,10 +762,11 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     // Fragment fm / fn adds a whole number of 16-row blocks, which leaves the
     // swizzles (they depend on the row modulo 16) unchanged: one base per depth
     // step plus immediate offsets.
-    uint32_t xo[4];
+    constexpr int G2_ND = 4 / G2_WK;                      // depth steps a wave takes per stage
+    uint32_t xo[G2_ND];
 #pragma unroll
-    for (int d = 0; d < 4; d++)
-        xo[d] = g2_xoff(wm * G2_FM * 16 + lr, 4 * lg + d);
+    for (int dd = 0; dd < G2_ND; dd++)
+        xo[dd] = g2_xoff(wm * G2_FM * 16 + lr, 4 * lg + G2_ND * wk + dd);
     const uint32_t wo = g2_woff(wn * G2_FN * 16 + lr, lg);
 
     // Every stage slot issues its DMAs, past the end clamped to the last stage
@@ -780,13 +790,23 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
             if (s < se) {
                 const uint8_t *xb = s_xb[j], *wb = s_wb[j];
                 u32x4 wv[G2_FN];
-                lds_read4(wb, wo, wo + 1024, wo + 2048, wo + 3072, wv[0], wv[1], wv[2], wv[3]);
+                if constexpr (G2_WK == 1) {
+                    lds_read4(wb, wo, wo + 1024, wo + 2048, wo + 3072, wv[0], wv[1], wv[2], wv[3]);
+                } else {
+                    // this wave's two words of each fragment (depth steps 2 wk, 2 wk + 1)
 #pragma unroll
-                for (int d = 0; d < 4; d++) {
+                    for (int fn = 0; fn < G2_FN; fn++) {
+                        const uint2 w2 = *reinterpret_cast<const uint2 *>(wb + wo + 1024 * fn + 8 * wk);
+                        wv[fn] = u32x4{w2.x, w2.y, 0u, 0u};
+                    }
+                }
+#pragma unroll
+                for (int dd = 0; dd < G2_ND; dd++) {
+                    const int d = G2_ND * wk + dd;
                     u32x4 xf[G2_FM];
 #pragma unroll
                     for (int fm = 0; fm < G2_FM; fm++)
-                        xf[fm] = *reinterpret_cast<const u32x4 *>(xb + xo[d] + 4096 * fm);
+                        xf[fm] = *reinterpret_cast<const u32x4 *>(xb + xo[dd] + 4096 * fm);
                     if (d == wn) {
 #pragma unroll
                         for (int fm = 0; fm < G2_FM; fm++)
@@ -794,15 +814,15 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
                     }
 #pragma unroll
                     for (int fn = 0; fn < G2_FN; fn++) {
-                        const u32x4 wa = unpack8(wv[fn][d]);
+                        const u32x4 wa = unpack8(wv[fn][dd]);
                         // Two waves a SIMD: the one issuing MFMAs goes first, so
                         // the other's LDS reads and unpacking fill the gaps.
-                        if (G2_WM == 2)
+                        if (G2_WM * G2_WK == 2)
                             __builtin_amdgcn_s_setprio(1);
 #pragma unroll
                         for (int fm = 0; fm < G2_FM; fm++)
                             acc[fn][fm] = mfma16(wa, xf[fm], acc[fn][fm]);
-                        if (G2_WM == 2)
+                        if (G2_WM * G2_WK == 2)
                             __builtin_amdgcn_s_setprio(0);
                     }
                 }
@@ -811,9 +831,36 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
     }
     wait_vmcnt<0>();                                          // the clamped tail DMAs
 
-    // Per-token activation sums: this wave column's quarter (every output row of
-    // the ones-MFMA holds the same sum), then the four quarters in order.
-    if (lg == 0) {
+    if constexpr (G2_WK == 2) {
+        // the second wave of each column adds its sums into the first's (through
+        // the stage buffers, free once every wave is past the main loop)
+        __syncthreads();
+        static_assert(G2_FN * G2_FM * 64 * 16 <= G2_XB && G2_FN * G2_FM * 64 * 16 <= G2_WB, "exchange");
+        f32x4 *e = reinterpret_cast<f32x4 *>(wn == 0 ? s_x0 : wn == 1 ? s_x1 : wn == 2 ? s_x2 : s_w0);
+        if (wk == 1) {
+#pragma unroll
+            for (int fn = 0; fn < G2_FN; fn++)
+#pragma unroll
+                for (int fm = 0; fm < G2_FM; fm++)
+                    e[(fn * G2_FM + fm) * 64 + lane] = acc[fn][fm];
+        }
+        // the activation-sum quarter wn was formed by the wave that took step wn
+        if (lg == 0 && wk == wn / 2) {
+#pragma unroll
+            for (int fm = 0; fm < G2_FM; fm++)
+                s_rsp[wn][fm * 16 + lr] = rsq[fm][0];
+        }
+        __syncthreads();
+        // Only the first wave of each column carries on, except through the
+        // fused EC's v staging, whose barriers every wave takes part in.
+        if (EC != 2 && wk == 1)
+            return;
+#pragma unroll
+        for (int fn = 0; fn < G2_FN; fn++)
+#pragma unroll
+            for (int fm = 0; fm < G2_FM; fm++)
+                acc[fn][fm] += e[(fn * G2_FM + fm) * 64 + lane];
+    } else if (lg == 0) {
 #pragma unroll
         for (int fm = 0; fm < G2_FM; fm++)
             s_rsp[wn][(wm * G2_FM + fm) * 16 + lr] = rsq[fm][0];
@@ -822,7 +869,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
         s_tagg = epoch_tag(claimed + opaque_zero64());
         s_tbad = 0;
     }
-    __syncthreads();
+    if constexpr (G2_WK == 1 || EC == 2)
+        __syncthreads();                                      // (the depth split synchronised s_rsp)
 
     // Epilogue: scale and offset removal, the EC term, store.
 #pragma unroll
@@ -964,6 +1012,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM) void gemm2_kernel(const LinearA
             }
         }
     }
+    if (G2_WK == 2 && wk == 1)
+        return;                                               // the column's first wave stores
     if (SPLIT) {
         // the scaled partial tile of this slice: unit-major, row-major bm x 256
         float *part = reinterpret_cast<float *>(a.ws + a.L.gpart) + unit * (G2_BM * G2_BN);
@@ -1065,16 +1115,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
     }
 }
 
-template <int WM, int FM, int EC>
+template <int WM, int FM, int EC, int WK = 1>
 hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
 {
     const int64_t bm = 16 * FM * WM;
     const int64_t ntiles = ((a.N + G2_BN - 1) / G2_BN) * ((a.M + bm - 1) / bm);
-    const dim3 block(64 * G2_WN * WM);
+    const dim3 block(64 * G2_WN * WM * WK);
     if (EC == 2 || a.g_ks > 1) {
         // EC == 2 (K split only): the pre-pass blocks come first in the grid
         const int64_t pre = EC == 2 ? a.npre : 0;
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1>), dim3((unsigned)(pre + ntiles * a.g_ks)),
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1, WK>), dim3((unsigned)(pre + ntiles * a.g_ks)),
                            block, 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -1090,9 +1140,9 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
     }
     if constexpr (EC != 2) {
         if (a.out_f32)
-            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1>), dim3((unsigned)ntiles), block, 0, s, a);
+            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1, WK>), dim3((unsigned)ntiles), block, 0, s, a);
         else
-            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0>), dim3((unsigned)ntiles), block, 0, s, a);
+            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0, WK>), dim3((unsigned)ntiles), block, 0, s, a);
     }
     return hipGetLastError();
 }
@@ -1116,8 +1166,8 @@ hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStrea
     (void)force_large;                                    // a.g_bm and a.g_ks carry the choice
     if (a.g_bm == 64) {
         if (ec_on == 2)
-            return launch_gemm2_t<1, 4, 2>(a, s);
-        return ec_on ? launch_gemm2_t<1, 4, 1>(a, s) : launch_gemm2_t<1, 4, 0>(a, s);
+            return launch_gemm2_t<1, 4, 2, 2>(a, s);
+        return ec_on ? launch_gemm2_t<1, 4, 1, 2>(a, s) : launch_gemm2_t<1, 4, 0, 2>(a, s);
     }
     if (ec_on == 2)
         return launch_gemm2_t<2, 4, 2>(a, s);
