@@ -681,21 +681,25 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
         wsrc[j] = a.packed + nn * (K / 2) + 16 * c;
         wlast[j] = (K - 32 * c + 127) / 128 - 1;          // last stage with 128 st + 32 c < K
     }
+    auto issue_x = [&](int64_t st, uint8_t *xbase, int j) {
+        const void *src = st < xlim[j] ? (const void *)(xsrc[j] + 256 * st) : (const void *)zsrc;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
+                                         (__attribute__((address_space(3))) void *)(xbase + 1024 * (G2_XI * wave + j)),
+                                         16, 0, 0);
+    };
+    auto issue_w = [&](int64_t st, uint8_t *wbase, int j) {
+        const int64_t sw = st < wlast[j] ? st : wlast[j];
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(wsrc[j] + 64 * sw),
+                                         (__attribute__((address_space(3))) void *)(wbase + 1024 * (G2_WI * wave + j)),
+                                         16, 0, 0);
+    };
     auto issue = [&](int64_t st, uint8_t *xbase, uint8_t *wbase) {
 #pragma unroll
-        for (int j = 0; j < G2_XI; j++) {
-            const void *src = st < xlim[j] ? (const void *)(xsrc[j] + 256 * st) : (const void *)zsrc;
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)src,
-                                             (__attribute__((address_space(3))) void *)(xbase + 1024 * (G2_XI * wave + j)),
-                                             16, 0, 0);
-        }
+        for (int j = 0; j < G2_XI; j++)
+            issue_x(st, xbase, j);
 #pragma unroll
-        for (int j = 0; j < G2_WI; j++) {
-            const int64_t sw = st < wlast[j] ? st : wlast[j];
-            __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(wsrc[j] + 64 * sw),
-                                             (__attribute__((address_space(3))) void *)(wbase + 1024 * (G2_WI * wave + j)),
-                                             16, 0, 0);
-        }
+        for (int j = 0; j < G2_WI; j++)
+            issue_w(st, wbase, j);
     };
 
     // EC operands of one 32-rank chunk t: v (hi, lo) of this wave's tokens and
@@ -786,10 +790,18 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
             wait_vmcnt<G2_WAIT>();                            // this wave's part of stage s
             bare_barrier();                                   // every wave's part; stage s - 1 free
             const int64_t sn = (s + G2_STAGES - 1 < slast) ? s + G2_STAGES - 1 : slast;
-            issue(sn, s_xb[(j + G2_STAGES - 1) % G2_STAGES], s_wb[(j + G2_STAGES - 1) % G2_STAGES]);
-            if (s < se) {
-                const uint8_t *xb = s_xb[j], *wb = s_wb[j];
-                u32x4 wv[G2_FN];
+            // The next stage's DMAs are spread over this stage's depth steps
+            // (one or two before each step's MFMAs) rather than issued all at
+            // once, so no wave stalls on a burst of DMA issue while it has MFMAs
+            // ready.  Every slot issues all of them, also past the slice's end,
+            // outside any branch: the compiler then tracks exactly which stage
+            // each outstanding DMA fills.
+            uint8_t *const nxb = s_xb[(j + G2_STAGES - 1) % G2_STAGES];
+            uint8_t *const nwb = s_wb[(j + G2_STAGES - 1) % G2_STAGES];
+            const bool live = s < se;
+            const uint8_t *xb = s_xb[j], *wb = s_wb[j];
+            u32x4 wv[G2_FN];
+            if (live) {
                 if constexpr (G2_WK == 1) {
                     lds_read4(wb, wo, wo + 1024, wo + 2048, wo + 3072, wv[0], wv[1], wv[2], wv[3]);
                 } else {
@@ -800,8 +812,14 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                         wv[fn] = u32x4{w2.x, w2.y, 0u, 0u};
                     }
                 }
+            }
 #pragma unroll
-                for (int dd = 0; dd < G2_ND; dd++) {
+            for (int dd = 0; dd < G2_ND; dd++) {
+                if (dd < G2_XI)
+                    issue_x(sn, nxb, dd);
+                if (dd < G2_WI)
+                    issue_w(sn, nwb, dd);
+                if (live) {
                     const int d = G2_ND * wk + dd;
                     u32x4 xf[G2_FM];
 #pragma unroll
@@ -827,6 +845,12 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                     }
                 }
             }
+#pragma unroll
+            for (int jj = G2_ND; jj < G2_XI; jj++)
+                issue_x(sn, nxb, jj);
+#pragma unroll
+            for (int jj = G2_ND; jj < G2_WI; jj++)
+                issue_w(sn, nwb, jj);
         }
     }
     wait_vmcnt<0>();                                          // the clamped tail DMAs
