@@ -387,7 +387,9 @@ def run_c5(args, torch, sp, gen):
     xs = {K: dev(gen.make_c5(0, "down" if K == gen.C5_FF else "q", M)["x"], torch)
           for K in (gen.C5_D, gen.C5_FF)}
     ys = {N: torch.empty((M, N), dtype=torch.float32, device="cuda") for N in (gen.C5_D, gen.C5_FF)}
-    wsp = sp.new_workspace(M, gen.C5_FF, gen.C5_FF, 32)
+    # one workspace for every layer: the largest any of their shapes needs
+    need = max(sp.spear_w4_linear_workspace_size(M, N, K, r) for (N, K, _, _, r) in layers)
+    wsp = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
 
     def steps_fn(use_ec):
         def record(n):

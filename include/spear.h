@@ -147,7 +147,10 @@ spear_status spear_gate(const spear_bf16 *x, int64_t M, int64_t K, const spear_b
 
 /*
  * spear_w4_linear_workspace_size -- bytes of workspace spear_w4_linear needs
- * for these sizes (r = 0 when there is no EC).  Host-only, no HIP call.
+ * for these sizes (r = 0 when there is no EC).  Host-only, no HIP call.  The
+ * size serves every smaller M with the same N, K and r; it is not monotone in
+ * N or K (the GEMM's K split depends on the layer's shape), so a workspace
+ * shared by layers of several shapes takes the largest of their sizes.
  */
 size_t spear_w4_linear_workspace_size(int64_t M, int64_t N, int64_t K, int32_t r);
 

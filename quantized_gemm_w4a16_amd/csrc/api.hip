@@ -41,17 +41,19 @@ static int64_t ec_producers(int64_t mr, int64_t K, int64_t rpad, int64_t *prod_k
     return cdiv(K, DEC_WAVES * *prod_k);
 }
 
-// MFMA GEMM tiling: tokens per tile, and the K slices a tile is split into so
-// that about 256 workgroups run, each over at least 4 stages of 128 (one slice
-// when the path takes whole tiles).
-static int64_t gemm_bm(int64_t M, int whole) { return (!whole && M <= 64) ? 64 : 128; }
+// MFMA GEMM tiling: tokens and channels per tile, and the K slices a tile is
+// split into so that about 256 workgroups run, each over at least 4 stages of
+// 128 (one slice when the path takes whole tiles).  Up to 128 tokens the tile
+// is 64 x 64, so that narrow layers fill the chip with few or no K slices.
+static int64_t gemm_bm(int64_t M, int whole) { return (!whole && M <= 128) ? 64 : 128; }
+static int64_t gemm_bn(int64_t bm) { return bm == 64 ? 64 : 256; }
 
 static int64_t gemm_ks(int64_t M, int64_t N, int64_t K, int whole)
 {
     if (whole)
         return 1;
     const int64_t bm = gemm_bm(M, 0);
-    const int64_t tiles = cdiv(N, 256) * cdiv(M > 0 ? M : 1, bm);
+    const int64_t tiles = cdiv(N, gemm_bn(bm)) * cdiv(M > 0 ? M : 1, bm);
     const int64_t most = cdiv(K, 128) / 4;
     int64_t ks = 256 / tiles;
     ks = ks < most ? ks : most;
@@ -59,18 +61,21 @@ static int64_t gemm_ks(int64_t M, int64_t N, int64_t K, int whole)
 }
 
 // Bytes of fp32 partial tiles a split GEMM writes for M tokens: one
-// bm x 256 tile per (slice, tile).  The region is sized for the most any token
+// bm x bn tile per (slice, tile).  The region is sized for the most any token
 // count up to M needs, so that a workspace sized for M serves every smaller M.
 static size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K)
 {
     auto need = [&](int64_t m) -> size_t {
-        const int64_t ks = gemm_ks(m, N, K, 0), bm = gemm_bm(m, 0);
-        return ks > 1 ? (size_t)(ks * cdiv(N, 256) * cdiv(m, bm) * bm * 256) * sizeof(float) : 0;
+        const int64_t ks = gemm_ks(m, N, K, 0), bm = gemm_bm(m, 0), bn = gemm_bn(bm);
+        return ks > 1 ? (size_t)(ks * cdiv(N, bn) * cdiv(m, bm) * bm * bn) * sizeof(float) : 0;
     };
     const int64_t m1 = M < 1 ? 1 : M;
     size_t best = need(m1 < 64 ? m1 : 64);            // up to 64 tokens: one 64-token tile row
     if (m1 > 64) {
-        for (int64_t tm = 1;; tm++) {                 // tm rows of 128-token tiles
+        best = need(m1 < 128 ? m1 : 128);             // up to 128 tokens: two 64-token tile rows
+        for (int64_t tm = 2;; tm++) {                 // tm rows of 128-token tiles
+            if (128 * (tm - 1) >= m1)
+                break;
             const int64_t m = 128 * tm < m1 ? 128 * tm : m1;
             const size_t b = need(m);
             best = b > best ? b : best;
@@ -378,6 +383,7 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
         a.pre_ks = ks;
     }
     a.g_bm = gemm_bm(M, path == SPEAR_PATH_PREFILL_LARGE);
+    a.g_bn = gemm_bn(a.g_bm);
     a.g_ks = gemm_ks(M, N, K, path == SPEAR_PATH_PREFILL_LARGE);
     a.L = L;
     a.out_f32 = out_dtype == SPEAR_OUT_F32;
@@ -412,13 +418,14 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
             e = launch_decode(a, ec ? 2 : 0, s);
         break;
     default:
-        if (ec && a.g_ks > 1 && cdiv(M, 16) < PRE_GROUPS) {
-            // K-split GEMM: the pre-pass runs as the first blocks of the GEMM's
-            // launch, on the CUs the GEMM's tiles leave free, and the epilogues
-            // wait for its tagged v.  About that many pre-pass workgroups (at
-            // least 32), each of its waves over at least one step of 32.
+        if (ec && (a.g_ks > 1 || a.g_bm == 64) && cdiv(M, 16) < PRE_GROUPS) {
+            // Few GEMM tiles (a K split, or 64 x 64 tiles): the pre-pass runs as
+            // the first blocks of the GEMM's launch, on the CUs the GEMM's tiles
+            // leave free, and the epilogues wait for its tagged v.  About that
+            // many pre-pass workgroups (at least 32), each of its waves over at
+            // least one step of 32.
             const int64_t tg = cdiv(M, 16), T = K / 32, pw = 8;   // the GEMM's 8 waves
-            const int64_t gwg = cdiv(N, 256) * cdiv(M, a.g_bm) * a.g_ks;
+            const int64_t gwg = cdiv(N, a.g_bn) * cdiv(M, a.g_bm) * a.g_ks;
             const int64_t room = gwg < 256 - 32 ? 256 - gwg : 32;
             int64_t ks = cdiv(room, tg);
             const int64_t most = T / pw > 0 ? T / pw : 1;

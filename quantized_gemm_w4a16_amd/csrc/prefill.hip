@@ -549,15 +549,14 @@ __global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
 // constant-one operand per token fragment: wave column c takes the 8-deep
 // quarter c of every 32-deep step, so the extra work is spread evenly.
 //
-// Few tiles (small M): K is split into a.g_ks slices, one workgroup each, so
-// that about 256 workgroups run; a workgroup stores its scaled partial tile
-// (the EC term in slice 0 only) and a second launch (splitk_reduce_kernel)
-// adds the slices in order.  Up to 64 tokens the tile is 256 x 64 with one
-// wave per SIMD, so each weight fragment is unpacked once per workgroup.
-constexpr int G2_WN = 4, G2_FN = 4;
-constexpr int G2_BN = 16 * G2_FN * G2_WN;                 // 256 channels
+// Few tiles: K is split into a.g_ks slices, one workgroup each, so that about
+// 256 workgroups run; a workgroup stores its scaled partial tile (with its
+// share of the EC's rank chunks) and a second launch (splitk_reduce_kernel)
+// adds the slices in order.  Up to 128 tokens the tile is 64 x 64 (eight
+// waves: 2 along the tokens x 2 along the channels x 2 along the depth of each
+// stage), which fills the chip on narrow layers with few or no K slices.
 constexpr int G2_STAGES = 3;
-constexpr int G2_WB = G2_BN * 64;                         // packed weight bytes of one stage
+constexpr int G2_WBA = 256 * 64;                          // bytes of a 256-channel weight stage
 
 // LDS byte offsets: chunk c (0..15) of activation row r, chunk c (0..3) of weight row r.
 __device__ __forceinline__ uint32_t g2_xoff(int r, int c) { return r * 256 + ((c ^ (r & 15)) << 4); }
@@ -573,31 +572,51 @@ __device__ __forceinline__ void lds_read4(const uint8_t *base, uint32_t a0, uint
     r3 = *reinterpret_cast<const u32x4 *>(base + a3);
 }
 
-template <int G2_WM, int G2_FM, int SPLIT, int EC, int OUT_F32, int G2_WK = 1>
+template <int G2_WM, int G2_FM, int SPLIT, int EC, int OUT_F32, int G2_WK = 1, int G2_FN = 4, int G2_WN = 4>
 __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const LinearArgs a)
 {
-    // G2_WK = 2 (one token row of waves): two waves share each wave column, the
-    // first taking depth steps 0 and 1 of every 128-deep stage, the second 2
-    // and 3, so each SIMD holds two waves; the second adds its sums into the
-    // first's after the main loop.
-    static_assert(G2_WK == 1 || (G2_WK == 2 && G2_WM == 1), "depth split: 64-token tiles");
+    // G2_WK = 2 (64 x 64 tiles): two waves share each (token, channel) pair of
+    // fragments, the first taking depth steps 0 and 1 of every 128-deep stage,
+    // the second 2 and 3, so each SIMD holds two waves; the second adds its
+    // sums into the first's after the main loop.
+    static_assert((G2_WN == 4 && G2_FN == 4 && G2_WK == 1) ||
+                      (G2_WN == 2 && G2_FN == 2 && G2_WM == 2 && G2_FM == 2 && G2_WK == 2),
+                  "256-channel tiles, or 64 x 64 tiles with the depth split");
+    constexpr int G2_BN = 16 * G2_FN * G2_WN;             // channels: 256 or 64
+    constexpr int G2_WB = G2_BN * 64;                     // packed weight bytes of one stage
     constexpr int G2_NT = 64 * G2_WN * G2_WM * G2_WK;     // 256 or 512 threads
     constexpr int G2_BM = 16 * G2_FM * G2_WM;             // tokens
     constexpr int G2_XB = G2_BM * 256;                    // activation bytes of one stage
     constexpr int G2_XI = G2_XB / (G2_NT * 16);           // activation DMAs a lane, per stage
-    constexpr int G2_WI = G2_WB / (G2_NT * 16);           // weight DMAs a lane, per stage
-    static_assert(G2_XI * G2_NT * 16 == G2_XB && G2_WI * G2_NT * 16 == G2_WB, "stage split");
+    // Weight DMAs a lane, per stage, of G2_WS bytes each: a 64-channel stage
+    // (4 KB) is too small for one 16-byte DMA a lane, so every wave takes two
+    // 4-byte DMAs of it.  Every wave then issues the same DMAs (no branch), which
+    // keeps the compiler's tracking of the LDS DMAs exact: it waits for a stage's
+    // own DMAs only, never for all of them.
+    constexpr int G2_WS = G2_BN == 64 ? 4 : 16;
+    constexpr int G2_WI = G2_WB / (G2_NT * G2_WS);
+    static_assert(G2_XI * G2_NT * 16 == G2_XB && G2_WI * G2_NT * G2_WS == G2_WB, "stage split");
+    // Ring depth: a 64-channel stage is 20 KB, so its ring holds six stages,
+    // taken two at a time (four in flight, 120 KB of LDS); a 256-channel ring
+    // holds three.
+    constexpr int G2_ST = G2_BN == 64 ? 6 : G2_STAGES;
+    constexpr int G2_WBS = G2_BN == 64 ? G2_WB : G2_WBA; // bytes of a weight stage buffer
     __shared__ __attribute__((aligned(16))) uint8_t s_x0[G2_XB];
     __shared__ __attribute__((aligned(16))) uint8_t s_x1[G2_XB];
     __shared__ __attribute__((aligned(16))) uint8_t s_x2[G2_XB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_w0[G2_WB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_w1[G2_WB];
-    __shared__ __attribute__((aligned(16))) uint8_t s_w2[G2_WB];
-    __shared__ float s_rsp[G2_WN][G2_BM];     // activation-sum quarters
-    static_assert(G2_STAGES == 3, "one LDS object per stage");
-    static_assert(G2_WN == 4 && G2_FN == 4, "one 8-deep quarter per wave column; 4 weight fragments");
-    uint8_t *const s_xb[G2_STAGES] = {s_x0, s_x1, s_x2};
-    uint8_t *const s_wb[G2_STAGES] = {s_w0, s_w1, s_w2};
+    __shared__ __attribute__((aligned(16))) uint8_t s_x3[G2_ST > 3 ? G2_XB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x4[G2_ST > 4 ? G2_XB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_x5[G2_ST > 5 ? G2_XB : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w0[G2_WBS];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w1[G2_WBS];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w2[G2_WBS];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w3[G2_ST > 3 ? G2_WBS : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w4[G2_ST > 4 ? G2_WBS : 16];
+    __shared__ __attribute__((aligned(16))) uint8_t s_w5[G2_ST > 5 ? G2_WBS : 16];
+    __shared__ float s_rsp[4][G2_BM];         // activation sums of the four 32-deep steps
+    static_assert(G2_ST == 3 || G2_ST == 6, "one LDS object per stage");
+    uint8_t *const s_xb[6] = {s_x0, s_x1, s_x2, s_x3, s_x4, s_x5};
+    uint8_t *const s_wb[6] = {s_w0, s_w1, s_w2, s_w3, s_w4, s_w5};
 
     __shared__ uint32_t s_tagg, s_tbad;
     pin_args(a);
@@ -612,22 +631,26 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
             claimed = epoch_claim(a);
         if ((int64_t)blockIdx.x < a.npre) {
             // u: waves 0 .. PW/2 - 1 in s_x0, the others in s_x1; the workgroup's u in
-            // s_x2; logit partials and w_g in s_w0; the small arrays in s_w1.
+            // s_x2; logit partials and w_g in c0 (s_w0, or s_x3 when the
+            // weight buffers are small); the small arrays in c1 (s_w1 or s_x4).
             constexpr int PW = G2_NT / 64;
+            constexpr int CB = G2_ST > 4 ? G2_XB : G2_WBS;
             static_assert((PW / 2) * PRE_RT * 64 * 16 <= G2_XB && PRE_TILES * 64 * 16 <= G2_XB &&
-                          PW * 64 * 8 + PW * 4 * PRE_T * 16 <= G2_WB && 16 * 16 + 8 <= G2_WB,
+                          PW * 64 * 8 + PW * 4 * PRE_T * 16 <= CB && 16 * 16 + 8 <= CB,
                           "pre-pass LDS inside the stage buffers");
+            uint8_t *const c0 = G2_ST > 4 ? s_x3 : s_w0;
+            uint8_t *const c1 = G2_ST > 4 ? s_x4 : s_w1;
             const PreShared<PW> sh = {
                 reinterpret_cast<f32x4(*)[PRE_RT][64]>(s_x0),
                 reinterpret_cast<f32x4(*)[PRE_RT][64]>(s_x1),
-                reinterpret_cast<double(*)[64]>(s_w0),
-                reinterpret_cast<u32x4(*)[4 * PRE_T]>(s_w0 + PW * 64 * 8),
+                reinterpret_cast<double(*)[64]>(c0),
+                reinterpret_cast<u32x4(*)[4 * PRE_T]>(c0 + PW * 64 * 8),
                 reinterpret_cast<f32x4(*)[64]>(s_x2),
-                reinterpret_cast<double *>(s_w1),
-                reinterpret_cast<float *>(s_w1 + 128),
-                reinterpret_cast<int *>(s_w1 + 192),
-                reinterpret_cast<uint32_t *>(s_w1 + 256),
-                reinterpret_cast<uint32_t *>(s_w1 + 260)};
+                reinterpret_cast<double *>(c1),
+                reinterpret_cast<float *>(c1 + 128),
+                reinterpret_cast<int *>(c1 + 192),
+                reinterpret_cast<uint32_t *>(c1 + 256),
+                reinterpret_cast<uint32_t *>(c1 + 260)};
             if ((int64_t)blockIdx.x < ((a.M + 15) / 16) * a.pre_ks)
                 prepass_body<PW>(a, blockIdx.x, sh, claimed, true);
             return;
@@ -658,8 +681,9 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     // 4 (G2_XI w + j) .. +3, lane i the slot i of that 1 KB (chunk (i % 16) ^
     // (row % 16) of its row); rows past M repeat row M - 1 (never stored).
     // Weights: instruction j fills rows 16 (G2_WI w + j) .. +15, lane i the slot
-    // i of that 1 KB (chunk (i % 4) ^ ((row / 2) % 4)); rows past N repeat the
-    // last row.  Each lane's stage-0 source and the number of stages its chunk
+    // i of that 1 KB (chunk (i % 4) ^ ((row / 2) % 4)); with 4-byte DMAs rows
+    // 4 (G2_WI w + j) .. +3, lane i word i % 4 of slot i / 4.  Rows past N repeat
+    // the last row.  Each lane's stage-0 source and the number of stages its chunk
     // stays inside K are computed once.  Activation chunks past K come from the
     // zero block; weight chunks past K re-read the lane's last chunk inside K
     // (finite values that meet zero activations).
@@ -675,10 +699,11 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     }
 #pragma unroll
     for (int j = 0; j < G2_WI; j++) {
-        const int r = 16 * (G2_WI * wave + j) + (lane >> 2);
-        const int c = (lane & 3) ^ ((r >> 1) & 3);
+        const int slot = G2_WS == 16 ? lane : lane >> 2;  // 16-byte slot of the 1 KB or 256 B
+        const int r = (G2_WS == 16 ? 16 : 4) * (G2_WI * wave + j) + (slot >> 2);
+        const int c = (slot & 3) ^ ((r >> 1) & 3);
         const int64_t nn = n0 + r < N ? n0 + r : N - 1;
-        wsrc[j] = a.packed + nn * (K / 2) + 16 * c;
+        wsrc[j] = a.packed + nn * (K / 2) + 16 * c + (G2_WS == 16 ? 0 : 4 * (lane & 3));
         wlast[j] = (K - 32 * c + 127) / 128 - 1;          // last stage with 128 st + 32 c < K
     }
     auto issue_x = [&](int64_t st, uint8_t *xbase, int j) {
@@ -689,9 +714,12 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     };
     auto issue_w = [&](int64_t st, uint8_t *wbase, int j) {
         const int64_t sw = st < wlast[j] ? st : wlast[j];
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(wsrc[j] + 64 * sw),
-                                         (__attribute__((address_space(3))) void *)(wbase + 1024 * (G2_WI * wave + j)),
-                                         16, 0, 0);
+        const auto *src = (const __attribute__((address_space(1))) void *)(wsrc[j] + 64 * sw);
+        auto *dst = (__attribute__((address_space(3))) void *)(wbase + 64 * G2_WS * (G2_WI * wave + j));
+        if constexpr (G2_BN == 64)
+            __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+        else
+            __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
     };
     auto issue = [&](int64_t st, uint8_t *xbase, uint8_t *wbase) {
 #pragma unroll
@@ -729,7 +757,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
         ec_load((int)ks, pvh, pvl, pbf);
     // EC == 2, one wave a SIMD: the B rows of the slice's first rank chunk now
     // (v comes from this launch's pre-pass blocks, at the end).
-    if (EC == 2 && G2_WM == 1 && ks < a.rpad / 32) {
+    constexpr bool PBF = G2_BN == 64;                     // registers to spare
+    if (EC == 2 && PBF && ks < a.rpad / 32) {
         const int j = 32 * (int)ks + 8 * lg;
 #pragma unroll
         for (int fn = 0; fn < G2_FN; fn++) {
@@ -751,13 +780,13 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
             zb_raw[fn][i] = load_zero_byte(a.zeros, a.scales, nn);
         }
 
-    f32x4 acc[G2_FN][G2_FM], rsq[G2_FM];
+    f32x4 acc[G2_FN][G2_FM], acc1[G2_FN][G2_FM], rsq[G2_FM];
     const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
 #pragma unroll
     for (int fn = 0; fn < G2_FN; fn++)
 #pragma unroll
         for (int fm = 0; fm < G2_FM; fm++)
-            acc[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[fn][fm] = acc1[fn][fm] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int fm = 0; fm < G2_FM; fm++)
         rsq[fm] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -773,94 +802,156 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
         xo[dd] = g2_xoff(wm * G2_FM * 16 + lr, 4 * lg + G2_ND * wk + dd);
     const uint32_t wo = g2_woff(wn * G2_FN * 16 + lr, lg);
 
-    // Every stage slot issues its DMAs, past the end clamped to the last stage
-    // (never used), so each wave always has exactly one further stage in flight
-    // when it waits for the current one.
-    const int64_t slast = se - 1;
+    // This wave's W words of one stage (wb).
+    auto wread = [&](const uint8_t *wb, u32x4 *wv) {
+        if constexpr (G2_WK == 1) {
+            lds_read4(wb, wo, wo + 1024, wo + 2048, wo + 3072, wv[0], wv[1], wv[2], wv[3]);
+        } else {
+            // this wave's two words of each fragment (depth steps 2 wk, 2 wk + 1)
 #pragma unroll
-    for (int j = 0; j < G2_STAGES - 1; j++)
-        issue(sb + j < slast ? sb + j : slast, s_xb[j], s_wb[j]);
-    constexpr int G2_WAIT = (G2_XI + G2_WI) * (G2_STAGES - 2);
-    static_assert(G2_WAIT < 64, "vmcnt");
+            for (int fn = 0; fn < G2_FN; fn++) {
+                const uint2 w2 = *reinterpret_cast<const uint2 *>(wb + wo + 1024 * fn + 8 * wk);
+                wv[fn] = u32x4{w2.x, w2.y, 0u, 0u};
+            }
+        }
+    };
+    // Depth step dd of one stage (xb, wv) into the accumulator set ac.
+    auto step = [&](const uint8_t *xb, const u32x4 *wv, int dd, f32x4 (&ac)[G2_FN][G2_FM]) {
+        const int d = G2_ND * wk + dd;
+        u32x4 xf[G2_FM];
+#pragma unroll
+        for (int fm = 0; fm < G2_FM; fm++)
+            xf[fm] = *reinterpret_cast<const u32x4 *>(xb + xo[dd] + 4096 * fm);
+        if (d % G2_WN == wn) {                                // one wave column a step
+#pragma unroll
+            for (int fm = 0; fm < G2_FM; fm++)
+                rsq[fm] = mfma16(ones, xf[fm], rsq[fm]);
+        }
+#pragma unroll
+        for (int fn = 0; fn < G2_FN; fn++) {
+            const u32x4 wa = unpack8(wv[fn][dd]);
+            // Two waves a SIMD: the one issuing MFMAs goes first, so the other's
+            // LDS reads and unpacking fill the gaps.
+            if (G2_NT == 512)
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int fm = 0; fm < G2_FM; fm++)
+                ac[fn][fm] = mfma16(wa, xf[fm], ac[fn][fm]);
+            if (G2_NT == 512)
+                __builtin_amdgcn_s_setprio(0);
+        }
+    };
 
-    for (int64_t s0 = sb; s0 < se; s0 += G2_STAGES) {
+    // Every stage slot issues its DMAs, past the end clamped to the last stage
+    // (never used), so each wave always has the same number of further stages
+    // in flight when it waits for the current ones.  The next stages' DMAs are
+    // spread over this stage's depth steps (one or two before each step's
+    // MFMAs) rather than issued all at once, so no wave stalls on a burst of
+    // DMA issue while it has MFMAs ready.  Every slot issues all of them, also
+    // past the slice's end, outside any branch: the compiler then tracks
+    // exactly which stage each outstanding DMA fills.
+    const int64_t slast = se - 1;
+    if constexpr (G2_ST == 6) {
+        // 64 x 64 tiles: the six slots are taken two at a time (256 deep a
+        // barrier; two pairs in flight).  Each depth step accumulates into its
+        // own set, so that back-to-back MFMAs do not wait on each other.
+        static_assert(G2_ND == 2 && G2_XI == 2 && G2_WI == 2, "pair schedule");
+        constexpr int G2_WAIT2 = (G2_XI + G2_WI) * 2;        // the next pair's DMAs
 #pragma unroll
-        for (int j = 0; j < G2_STAGES; j++) {
-            const int64_t s = s0 + j;
-            wait_vmcnt<G2_WAIT>();                            // this wave's part of stage s
-            bare_barrier();                                   // every wave's part; stage s - 1 free
-            const int64_t sn = (s + G2_STAGES - 1 < slast) ? s + G2_STAGES - 1 : slast;
-            // The next stage's DMAs are spread over this stage's depth steps
-            // (one or two before each step's MFMAs) rather than issued all at
-            // once, so no wave stalls on a burst of DMA issue while it has MFMAs
-            // ready.  Every slot issues all of them, also past the slice's end,
-            // outside any branch: the compiler then tracks exactly which stage
-            // each outstanding DMA fills.
-            uint8_t *const nxb = s_xb[(j + G2_STAGES - 1) % G2_STAGES];
-            uint8_t *const nwb = s_wb[(j + G2_STAGES - 1) % G2_STAGES];
-            const bool live = s < se;
-            const uint8_t *xb = s_xb[j], *wb = s_wb[j];
-            u32x4 wv[G2_FN];
-            if (live) {
-                if constexpr (G2_WK == 1) {
-                    lds_read4(wb, wo, wo + 1024, wo + 2048, wo + 3072, wv[0], wv[1], wv[2], wv[3]);
-                } else {
-                    // this wave's two words of each fragment (depth steps 2 wk, 2 wk + 1)
+        for (int j = 0; j < 4; j++)
+            issue(sb + j < slast ? sb + j : slast, s_xb[j], s_wb[j]);
+        for (int64_t s0 = sb; s0 < se; s0 += 6) {
 #pragma unroll
-                    for (int fn = 0; fn < G2_FN; fn++) {
-                        const uint2 w2 = *reinterpret_cast<const uint2 *>(wb + wo + 1024 * fn + 8 * wk);
-                        wv[fn] = u32x4{w2.x, w2.y, 0u, 0u};
+            for (int p = 0; p < 3; p++) {
+                const int64_t s = s0 + 2 * p;
+                wait_vmcnt<G2_WAIT2>();                       // this wave's part of stages s, s + 1
+                bare_barrier();                               // every wave's part; pair p - 1 free
+                const int64_t sn0 = (s + 4 < slast) ? s + 4 : slast, sn1 = (s + 5 < slast) ? s + 5 : slast;
+                uint8_t *const nx0 = s_xb[(2 * p + 4) % 6], *const nw0 = s_wb[(2 * p + 4) % 6];
+                uint8_t *const nx1 = s_xb[(2 * p + 5) % 6], *const nw1 = s_wb[(2 * p + 5) % 6];
+#pragma unroll
+                for (int h = 0; h < 2; h++) {
+                    const bool live = s + h < se;
+                    const uint8_t *xb = s_xb[2 * p + h], *wb = s_wb[2 * p + h];
+                    u32x4 wv[G2_FN];
+                    if (live)
+                        wread(wb, wv);
+#pragma unroll
+                    for (int dd = 0; dd < 2; dd++) {
+                        // the pair's eight DMAs, two before each of its four steps
+                        const int q = 2 * h + dd;
+                        if (q < 2) {
+                            issue_x(sn0, nx0, q);
+                            issue_w(sn0, nw0, q);
+                        } else {
+                            issue_x(sn1, nx1, q - 2);
+                            issue_w(sn1, nw1, q - 2);
+                        }
+                        if (live) {
+                            if (dd == 0)
+                                step(xb, wv, 0, acc);
+                            else
+                                step(xb, wv, 1, acc1);
+                        }
                     }
                 }
             }
+        }
+    } else {
 #pragma unroll
-            for (int dd = 0; dd < G2_ND; dd++) {
-                if (dd < G2_XI)
-                    issue_x(sn, nxb, dd);
-                if (dd < G2_WI)
-                    issue_w(sn, nwb, dd);
-                if (live) {
-                    const int d = G2_ND * wk + dd;
-                    u32x4 xf[G2_FM];
+        for (int j = 0; j < G2_ST - 1; j++)
+            issue(sb + j < slast ? sb + j : slast, s_xb[j], s_wb[j]);
+        constexpr int G2_WAIT = (G2_XI + G2_WI) * (G2_ST - 2);
+        static_assert(G2_WAIT < 64, "vmcnt");
+        for (int64_t s0 = sb; s0 < se; s0 += G2_ST) {
 #pragma unroll
-                    for (int fm = 0; fm < G2_FM; fm++)
-                        xf[fm] = *reinterpret_cast<const u32x4 *>(xb + xo[dd] + 4096 * fm);
-                    if (d == wn) {
+            for (int j = 0; j < G2_ST; j++) {
+                const int64_t s = s0 + j;
+                wait_vmcnt<G2_WAIT>();                        // this wave's part of stage s
+                bare_barrier();                               // every wave's part; stage s - 1 free
+                const int64_t sn = (s + G2_ST - 1 < slast) ? s + G2_ST - 1 : slast;
+                uint8_t *const nxb = s_xb[(j + G2_ST - 1) % G2_ST];
+                uint8_t *const nwb = s_wb[(j + G2_ST - 1) % G2_ST];
+                const bool live = s < se;
+                const uint8_t *xb = s_xb[j], *wb = s_wb[j];
+                u32x4 wv[G2_FN];
+                if (live)
+                    wread(wb, wv);
 #pragma unroll
-                        for (int fm = 0; fm < G2_FM; fm++)
-                            rsq[fm] = mfma16(ones, xf[fm], rsq[fm]);
-                    }
-#pragma unroll
-                    for (int fn = 0; fn < G2_FN; fn++) {
-                        const u32x4 wa = unpack8(wv[fn][dd]);
-                        // Two waves a SIMD: the one issuing MFMAs goes first, so
-                        // the other's LDS reads and unpacking fill the gaps.
-                        if (G2_WM * G2_WK == 2)
-                            __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-                        for (int fm = 0; fm < G2_FM; fm++)
-                            acc[fn][fm] = mfma16(wa, xf[fm], acc[fn][fm]);
-                        if (G2_WM * G2_WK == 2)
-                            __builtin_amdgcn_s_setprio(0);
-                    }
+                for (int dd = 0; dd < G2_ND; dd++) {
+                    if (dd < G2_XI)
+                        issue_x(sn, nxb, dd);
+                    if (dd < G2_WI)
+                        issue_w(sn, nwb, dd);
+                    if (live)
+                        step(xb, wv, dd, acc);
                 }
+#pragma unroll
+                for (int jj = G2_ND; jj < G2_XI; jj++)
+                    issue_x(sn, nxb, jj);
+#pragma unroll
+                for (int jj = G2_ND; jj < G2_WI; jj++)
+                    issue_w(sn, nwb, jj);
             }
-#pragma unroll
-            for (int jj = G2_ND; jj < G2_XI; jj++)
-                issue_x(sn, nxb, jj);
-#pragma unroll
-            for (int jj = G2_ND; jj < G2_WI; jj++)
-                issue_w(sn, nwb, jj);
         }
     }
     wait_vmcnt<0>();                                          // the clamped tail DMAs
+    if constexpr (G2_BN == 64) {
+#pragma unroll
+        for (int fn = 0; fn < G2_FN; fn++)
+#pragma unroll
+            for (int fm = 0; fm < G2_FM; fm++)
+                acc[fn][fm] += acc1[fn][fm];
+    }
 
     if constexpr (G2_WK == 2) {
-        // the second wave of each column adds its sums into the first's (through
-        // the stage buffers, free once every wave is past the main loop)
+        // the second wave of each (token, channel) pair adds its sums into the
+        // first's (through the stage buffers, free once every wave is past the
+        // main loop)
         __syncthreads();
-        static_assert(G2_FN * G2_FM * 64 * 16 <= G2_XB && G2_FN * G2_FM * 64 * 16 <= G2_WB, "exchange");
-        f32x4 *e = reinterpret_cast<f32x4 *>(wn == 0 ? s_x0 : wn == 1 ? s_x1 : wn == 2 ? s_x2 : s_w0);
+        static_assert(G2_FN * G2_FM * 64 * 16 <= G2_XB && G2_ST > 3, "exchange");
+        const int q = wm * G2_WN + wn;
+        f32x4 *e = reinterpret_cast<f32x4 *>(q == 0 ? s_x0 : q == 1 ? s_x1 : q == 2 ? s_x2 : s_x3);
         if (wk == 1) {
 #pragma unroll
             for (int fn = 0; fn < G2_FN; fn++)
@@ -868,14 +959,14 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                 for (int fm = 0; fm < G2_FM; fm++)
                     e[(fn * G2_FM + fm) * 64 + lane] = acc[fn][fm];
         }
-        // the activation-sum quarter wn was formed by the wave that took step wn
-        if (lg == 0 && wk == wn / 2) {
+        // this wave formed the activation sums of step 2 wk + wn
+        if (lg == 0) {
 #pragma unroll
             for (int fm = 0; fm < G2_FM; fm++)
-                s_rsp[wn][fm * 16 + lr] = rsq[fm][0];
+                s_rsp[2 * wk + wn][(wm * G2_FM + fm) * 16 + lr] = rsq[fm][0];
         }
         __syncthreads();
-        // Only the first wave of each column carries on, except through the
+        // Only the first wave of each pair carries on, except through the
         // fused EC's v staging, whose barriers every wave takes part in.
         if (EC != 2 && wk == 1)
             return;
@@ -932,7 +1023,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
 #pragma unroll
             for (int fn = 0; fn < G2_FN; fn++) {
                 const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
-                bf[fn] = (G2_WM == 1 && t == ks) ? pbf[fn]
+                bf[fn] = (PBF && t == ks) ? pbf[fn]
                          : (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
             }
             bool ok = true;
@@ -1093,15 +1184,15 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
 template <int OUT_F32>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
 {
-    const int64_t M = a.M, N = a.N, KS = a.g_ks, bm = a.g_bm;
+    const int64_t M = a.M, N = a.N, KS = a.g_ks, bm = a.g_bm, bn = a.g_bn;
     const int64_t nq = (N + 3) / 4;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= M * nq)
         return;
     const int64_t m = idx / nq, n = 4 * (idx % nq);
-    const int64_t tiles_n = (N + G2_BN - 1) / G2_BN, ntiles = tiles_n * ((M + bm - 1) / bm);
-    const int64_t tile = (m / bm) * tiles_n + n / G2_BN;
-    const int64_t off = (m % bm) * G2_BN + n % G2_BN;
+    const int64_t tiles_n = (N + bn - 1) / bn, ntiles = tiles_n * ((M + bm - 1) / bm);
+    const int64_t tile = (m / bm) * tiles_n + n / bn;
+    const int64_t off = (m % bm) * bn + n % bn;
     const f32x4 *part = reinterpret_cast<const f32x4 *>(a.ws + a.L.gpart);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
@@ -1109,7 +1200,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
 #pragma unroll
         for (int i = 0; i < CMB_U; i++)
             if (q0 + i < KS)
-                p[i] = part[(((q0 + i) * ntiles + tile) * bm * G2_BN + off) / 4];
+                p[i] = part[(((q0 + i) * ntiles + tile) * bm * bn + off) / 4];
 #pragma unroll
         for (int i = 0; i < CMB_U; i++)
             if (q0 + i < KS)
@@ -1139,16 +1230,16 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
     }
 }
 
-template <int WM, int FM, int EC, int WK = 1>
+template <int WM, int FM, int EC, int WK = 1, int FN = 4, int WN = 4>
 hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
 {
-    const int64_t bm = 16 * FM * WM;
-    const int64_t ntiles = ((a.N + G2_BN - 1) / G2_BN) * ((a.M + bm - 1) / bm);
-    const dim3 block(64 * G2_WN * WM * WK);
-    if (EC == 2 || a.g_ks > 1) {
-        // EC == 2 (K split only): the pre-pass blocks come first in the grid
-        const int64_t pre = EC == 2 ? a.npre : 0;
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1, WK>), dim3((unsigned)(pre + ntiles * a.g_ks)),
+    const int64_t bm = 16 * FM * WM, bn = 16 * FN * WN;
+    const int64_t ntiles = ((a.N + bn - 1) / bn) * ((a.M + bm - 1) / bm);
+    const dim3 block(64 * WN * WM * WK);
+    // EC == 2: the pre-pass blocks come first in the grid
+    const int64_t pre = EC == 2 ? a.npre : 0;
+    if (a.g_ks > 1) {
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1, WK, FN, WN>), dim3((unsigned)(pre + ntiles * a.g_ks)),
                            block, 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
@@ -1162,12 +1253,10 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
                                dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    if constexpr (EC != 2) {
-        if (a.out_f32)
-            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1, WK>), dim3((unsigned)ntiles), block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0, WK>), dim3((unsigned)ntiles), block, 0, s, a);
-    }
+    if (a.out_f32)
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1, WK, FN, WN>), dim3((unsigned)(pre + ntiles)), block, 0, s, a);
+    else
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0, WK, FN, WN>), dim3((unsigned)(pre + ntiles)), block, 0, s, a);
     return hipGetLastError();
 }
 
@@ -1187,11 +1276,11 @@ hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 
 hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStream_t s)
 {
-    (void)force_large;                                    // a.g_bm and a.g_ks carry the choice
+    (void)force_large;                                    // a.g_bm, a.g_bn, a.g_ks carry the choice
     if (a.g_bm == 64) {
         if (ec_on == 2)
-            return launch_gemm2_t<1, 4, 2, 2>(a, s);
-        return ec_on ? launch_gemm2_t<1, 4, 1, 2>(a, s) : launch_gemm2_t<1, 4, 0, 2>(a, s);
+            return launch_gemm2_t<2, 2, 2, 2, 2, 2>(a, s);
+        return ec_on ? launch_gemm2_t<2, 2, 1, 2, 2, 2>(a, s) : launch_gemm2_t<2, 2, 0, 2, 2, 2>(a, s);
     }
     if (ec_on == 2)
         return launch_gemm2_t<2, 4, 2>(a, s);

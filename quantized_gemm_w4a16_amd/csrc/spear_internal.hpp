@@ -161,6 +161,7 @@ struct LinearArgs {
     int64_t ncg, ksplit, spw, nprod, prod_k, mpad;
     int64_t pre_ks;  // EC pre-pass: K slices per token group
     int64_t g_bm;    // MFMA GEMM: tokens per tile (64 or 128)
+    int64_t g_bn;    // MFMA GEMM: channels per tile (64 with 64-token tiles, else 256)
     int64_t g_ks;    // MFMA GEMM: K slices per tile (partials reduced by a second launch)
     int64_t npre;    // K-split GEMM with the EC pre-pass in its launch: leading pre-pass blocks
     WsLayout L;
@@ -200,7 +201,7 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.idx_out); pin_arg(a.nact_out); pin_arg(a.thr); pin_arg(a.b); pin_arg(a.hard);
     pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
     pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
-    pin_arg(a.pre_ks); pin_arg(a.g_ks); pin_arg(a.npre); pin_arg(a.L.vtag); pin_arg(a.L.gpart); pin_arg(a.L.preu); pin_arg(a.L.prez);
+    pin_arg(a.pre_ks); pin_arg(a.g_ks); pin_arg(a.g_bn); pin_arg(a.npre); pin_arg(a.L.vtag); pin_arg(a.L.gpart); pin_arg(a.L.preu); pin_arg(a.L.prez);
     pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.splitp); pin_arg(a.L.pu);
     pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);

@@ -194,8 +194,8 @@ RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 25
           (17, 1000, 160, 40), (33, 24, 4096, 8), (100, 200, 544, 64), (130, 129, 1024, 32),
           (257, 300, 2080, 24), (200, 300, 352, 32), (129, 513, 192, 16),
           # K split over workgroups with a K tail and EC rank chunks spread over
-          # the slices, on both sides of the 64-token tile switch
-          (64, 260, 1184, 96), (65, 700, 1280, 48),
+          # the slices; 64 x 64 tiles up to 128 tokens, 128 x 256 above
+          (64, 260, 1184, 96), (65, 700, 1280, 48), (128, 2050, 1024, 32), (129, 300, 1024, 16),
           # rank 32 with at least 128 token groups: 64-token pre-pass blocks over
           # K slices, a partial last block and a ragged last slice
           (2100, 96, 1056, 24),
