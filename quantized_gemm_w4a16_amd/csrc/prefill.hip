@@ -529,11 +529,12 @@ __global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
 }
 
 // ------------------------------------------------------------------------ GEMM
-// Output tile 256 channels x 16 FM WM tokens: WM = 2 (128 tokens, 8 waves: 4
-// along the channels x 2 along the tokens) or WM = 1 (64 tokens, 4 waves); each
-// wave holds 64 channels x 16 FM tokens as 4 x FM MFMA tiles.  K advances in stages
-// of 128.  Both operands go HBM/L2 -> LDS by global_load_lds into a ring of
-// G2_STAGES stage buffers, so the only memory operations in flight are these
+// Output tile 16 FN WN channels x 16 FM WM tokens, 8 waves: 256 x 128 (4 wave
+// columns along the channels x 2 along the tokens, each wave 64 x 64 as 4 x 4
+// MFMA tiles), or 64 x 64 (2 x 2 waves, each 32 x 32 as 2 x 2 tiles, times 2
+// along the depth of each stage).  K advances in stages of 128.  Both operands
+// go HBM/L2 -> LDS by global_load_lds into a ring of stage buffers (3, or 6
+// taken two at a time), so the only memory operations in flight are these
 // DMAs: one stage is read while the next ones land.  Each wave waits for its
 // own part of a stage (vmcnt) and one barrier per stage makes every part
 // visible.  The stage buffers are separate LDS objects and nothing but the
