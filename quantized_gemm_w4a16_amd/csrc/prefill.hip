@@ -756,7 +756,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     u32x4 pvh[G2_FM], pvl[G2_FM], pbf[G2_FN];
     if (ECPRE && wk == 0 && ks < a.rpad / 32)
         ec_load((int)ks, pvh, pvl, pbf);
-    // EC == 2, one wave a SIMD: the B rows of the slice's first rank chunk now
+    // EC == 2, 64 x 64 tiles: the B rows of the slice's first rank chunk now
     // (v comes from this launch's pre-pass blocks, at the end).
     constexpr bool PBF = G2_BN == 64;                     // registers to spare
     if (EC == 2 && PBF && ks < a.rpad / 32) {
