@@ -79,12 +79,13 @@ typedef int32_t spear_status;
 #define SPEAR_PATH_AUTO          0 /* decode path for M <= 16, prefill path otherwise   */
 #define SPEAR_PATH_DECODE        1 /* M <= 16: one launch, EC fused into the epilogue   */
 #define SPEAR_PATH_PREFILL       2 /* any M: EC pre-pass, then the MFMA GEMM whose
-                                      epilogue applies the EC.  Up to 128 tokens
-                                      the tiles are 64 x 64 and the pre-pass runs
-                                      as the first blocks of the GEMM's launch;
-                                      above, 256 x 128.  With few output tiles K
-                                      is split and a second launch adds the
-                                      slices                                         */
+                                      epilogue applies the EC.  Tiles are 64 x 64
+                                      up to 128 tokens, 256 x 128 above.  With few
+                                      output tiles K is split and a second launch
+                                      adds the slices.  With 64 x 64 tiles or a K
+                                      split, and fewer than 2048 tokens, the
+                                      pre-pass runs as the first blocks of the
+                                      GEMM's launch                                  */
 #define SPEAR_PATH_DECODE_2PASS  3 /* M <= 16: EC pre-pass, then the decode kernel      */
 #define SPEAR_PATH_PREFILL_LARGE 4 /* any M: EC pre-pass, then the 256 x 128-tile MFMA
                                       GEMM over whole K (the prefill path's choice
