@@ -72,7 +72,8 @@ static size_t gemm_part_bytes(int64_t M, int64_t N, int64_t K)
     const int64_t m1 = M < 1 ? 1 : M;
     size_t best = need(m1 < 64 ? m1 : 64);            // up to 64 tokens: one 64-token tile row
     if (m1 > 64) {
-        best = need(m1 < 128 ? m1 : 128);             // up to 128 tokens: two 64-token tile rows
+        const size_t b2 = need(m1 < 128 ? m1 : 128);  // up to 128 tokens: two 64-token tile rows
+        best = b2 > best ? b2 : best;
         for (int64_t tm = 2;; tm++) {                 // tm rows of 128-token tiles
             if (128 * (tm - 1) >= m1)
                 break;

@@ -56,8 +56,12 @@ def test_workspace_size_monotone_in_tokens(lib):
     share one allocation): the size never decreases as M grows."""
     f = sp.spear_w4_linear_workspace_size
     for (N, K, r) in [(4096, 4096, 32), (1024, 11008, 64), (512, 2048, 256), (17, 96, 8),
-                      (4096, 32768, 32), (64, 4096, 0)]:
-        sizes = [f(M, N, K, r) for M in list(range(1, 40)) + [64, 128, 2048, 4096]]
+                      (4096, 32768, 32), (64, 4096, 0), (2048, 2048, 32), (8192, 2048, 32),
+                      (2048, 8192, 32), (14336, 4096, 64)]:
+        # across the tile switches (64-token tiles up to 128 tokens) and K splits
+        Ms = list(range(1, 40)) + [63, 64, 65, 96, 127, 128, 129, 150, 255, 256, 257, 300,
+                                   512, 1000, 2047, 2048, 2049, 4096]
+        sizes = [f(M, N, K, r) for M in Ms]
         assert all(b >= a for a, b in zip(sizes, sizes[1:])), (N, K, r, sizes)
 
 
