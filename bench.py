@@ -133,7 +133,7 @@ def cpu_baseline_c2(Ms, budget_s):
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     done_bytes, t_used, calls = 0.0, 0.0, 0
     cached = {}
-    while t_used < budget_s and calls < 60:
+    while t_used < budget_s and calls < 5000:
         M = Ms[calls % len(Ms)]
         if M not in cached:
             d = gen.make(2, M=M)
