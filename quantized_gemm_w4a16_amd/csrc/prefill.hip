@@ -1282,8 +1282,9 @@ hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStrea
 {
     (void)force_large;                                    // a.g_bm, a.g_bn, a.g_ks carry the choice
     if (a.g_bm == 64) {
-        // 64 x 64 tiles: a variant without the DMA-source clamps when K is a
-        // multiple of 128 (their per-lane selects cost about 8 % of the loop)
+        // Both tile shapes have a variant without the DMA-source clamps for K a
+        // multiple of 128 (their per-lane selects cost about 8 % of the 64 x 64
+        // loop).
         if (a.K % 128 == 0) {
             if (ec_on == 2)
                 return launch_gemm2_t<2, 2, 2, 2, 2, 2, 1>(a, s);
@@ -1292,6 +1293,11 @@ hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStrea
         if (ec_on == 2)
             return launch_gemm2_t<2, 2, 2, 2, 2, 2>(a, s);
         return ec_on ? launch_gemm2_t<2, 2, 1, 2, 2, 2>(a, s) : launch_gemm2_t<2, 2, 0, 2, 2, 2>(a, s);
+    }
+    if (a.K % 128 == 0) {
+        if (ec_on == 2)
+            return launch_gemm2_t<2, 4, 2, 1, 4, 4, 1>(a, s);
+        return ec_on ? launch_gemm2_t<2, 4, 1, 1, 4, 4, 1>(a, s) : launch_gemm2_t<2, 4, 0, 1, 4, 4, 1>(a, s);
     }
     if (ec_on == 2)
         return launch_gemm2_t<2, 4, 2>(a, s);
