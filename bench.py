@@ -1,26 +1,34 @@
 """Benchmark of the W4A16 + gated-EC linear layer on one MI355X.
 
-Default workload (C2, decode): K = N = 4096 (7B-class attention projection),
-int4 asymmetric per-channel weights with bf16 scales, EC rank 32 with a soft
-gate.  One step is one pass of the layer for each decode batch M in {1, 4, 8}
-(three calls of spear_w4_linear, each one fused launch).  The weights and EC
-factors rotate over 64 device copies (538 MB, more than twice the 256 MB
-Infinity Cache) so every call streams them from HBM.  The timed steps are
-captured once in a HIP graph and replayed, so host launch overhead stays out of
-the timed region; the time is taken with HIP events on the launch stream.
+Default run (the JSON line's `value`): workload C2, decode.  K = N = 4096
+(7B-class attention projection), int4 asymmetric per-channel weights with bf16
+scales, EC rank 32 with a soft gate.  One step is one pass of the layer for each
+decode batch M in {1, 4, 8} (three calls of spear_w4_linear, each one fused
+launch).  The weights and EC factors rotate over 64 device copies (538 MB, more
+than twice the 256 MB Infinity Cache) so every call streams them from HBM.  The
+K timed steps are captured once in a HIP graph; the graph is replayed
+`--replays` times (each replay exactly K steps, bracketed by synchronisation and
+timed with HIP events on the launch stream) and the median replay gives
+`ms_per_step`, with p10 / p90 beside it.  `value` is algorithmic bytes moved per
+second (packed weights, scales, zero points, EC factors and gate weights,
+activations in, fp32 outputs out), in GB/s.
 
-`value` is algorithmic bytes moved per second (packed weights, scales, zero
-points, EC factors and gate weights, activations in, fp32 outputs out), in GB/s.
-The line also carries the plain-W4 time of the same steps (EC overhead), the
-roofline of the decode kernel and the CPU oracle timed on a bounded sample.
+The same line also carries:
+  * the plain-W4 time of the same steps (EC overhead), and per M the average
+    launch time of the fused and the plain decode kernel (one graph per M);
+  * `roofline` of the fused decode kernel against 8 TB/s, plus the rate of a
+    plain streaming read of the same 64 rotating weight buffers (the same-size
+    read floor, `stream_floor_GBps`);
+  * `prefill`: workload C4 (M = N = K = 4096, Student-t activations, EC rank 32
+    soft gate): TFLOP/s with and without the EC, the EC overhead, the plain
+    GEMM's fraction of the 2.5 PFLOP/s bf16 peak, and the CPU oracle on a
+    sample of C4 outputs;
+  * `cpu_baseline`: the CPU oracle on whole C2 layer calls.
 
---workload c1 times the small layer (M = 16, K = N = 1024, rank 16; launch
-latency bound, reported in microseconds a call and GB/s); --workload c4 times
-the prefill configuration instead (M = N = K = 4096,
-TFLOP/s); --workload c3 the MLP up-projection at M = 64 (K = 4096, N = 14336,
-rank 64, hard gate); --workload c5 a 28-layer stack of a 1.5B-class decoder's
-seven linears (ECs on 4 layers) at --c5-m tokens, reporting the stack time
-and the EC share.  None of these is the default line.
+--workload c1|c3|c4|c5 times one other workload alone, same JSON contract
+(C1: M = 16, K = N = 1024, launch-latency bound; C3: M = 64, K = 4096,
+N = 14336, rank 64, hard gate; C4: prefill; C5: a 28-layer stack of a
+1.5B-class decoder's seven linears with ECs on 4 layers at --c5-m tokens).
 """
 from __future__ import annotations
 
@@ -46,13 +54,19 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--replays", type=int, default=7,
+                   help="timed replays of the K-step graph (median, p10, p90 reported)")
+    p.add_argument("--no-prefill", action="store_true",
+                   help="leave the C4 prefill object out of the default C2 line")
+    p.add_argument("--prefill-steps", type=int, default=20,
+                   help="layer calls per replay of the C4 prefill graph in the default line")
     p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     p.add_argument("--c5-m", type=int, default=1, choices=[1, 16, 128, 2048],
                    help="tokens per call of the C5 stack")
     p.add_argument("--copies", type=int, default=64)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0,
-                   help="approximate CPU time budget of the oracle sample")
+                   help="approximate CPU time budget of each oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="also run a plain device copy of known size (for counter scaling)")
     return p.parse_args()
@@ -104,8 +118,11 @@ def build_copies(d, copies, torch, sp):
     return ws, ecs
 
 
-def time_graph(torch, record_steps, steps):
-    """Capture `steps` steps in one graph, replay once untimed, then time one replay."""
+def time_graph(torch, record_steps, steps, replays):
+    """Capture `steps` steps in one graph, replay it once untimed, then time
+    `replays` replays (each exactly `steps` steps, synchronised on both sides,
+    HIP events on the replay stream).  -> dict of ms per step: median, p10, p90,
+    and every replay."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -115,14 +132,24 @@ def time_graph(torch, record_steps, steps):
     torch.cuda.current_stream().wait_stream(s)
     g.replay()
     torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    g.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    return t0.elapsed_time(t1), g
+    per = []
+    for _ in range(max(1, replays)):
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record()
+        g.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        per.append(t0.elapsed_time(t1) / steps)
+    a = np.array(per)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "all": [round(v, 6) for v in per]}
+
+
+def stats_ms(t, nd=6):
+    return {"replays": len(t["all"]), "median_ms_per_step": round(t["median"], nd),
+            "p10_ms_per_step": round(t["p10"], nd), "p90_ms_per_step": round(t["p90"], nd)}
 
 
 def cpu_baseline_c2(Ms, budget_s):
@@ -162,6 +189,49 @@ def copy_calibration(torch):
     return n
 
 
+def cpu_baseline_c4(budget_s):
+    """The oracle on sampled outputs of the C4 prefill layer (whole rows of the
+    fp64 dot products, the gate and the EC of each sampled token), until the
+    budget is used.  Rate: algorithmic flops of the sampled outputs (2 K for the
+    main term and 2 r for the EC up-projection per output, plus 2 K for the gate
+    and 2 K r for the EC down-projection per distinct token) per second."""
+    import oracle
+    from quantized_gemm_w4a16_amd import inputs as gen
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    d = gen.make(4)
+    packed, _ = oracle.pack_w4(d["codes"], d["kind"])
+    M, N, K, r = d["M"], d["N"], d["K"], d["ec"]["r"]
+    rng = np.random.default_rng(404)
+    flops, t_used, outs = 0.0, 0.0, 0
+    S = 4096
+    while t_used < budget_s and outs < 50_000_000:
+        m = rng.integers(0, M, 64)
+        ms = np.repeat(m, S // 64)
+        ns = rng.integers(0, N, S)
+        t = time.perf_counter()
+        oracle.w4_linear_sampled(d["x"], packed, d["scales"], d["zeros"], d["ec"], ms, ns)
+        t_used += time.perf_counter() - t
+        flops += S * (2.0 * K + 2.0 * r) + len(np.unique(m)) * (2.0 * K + 2.0 * K * r)
+        outs += S
+    return {"value": round(flops / t_used / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{outs} sampled C4 outputs (64 tokens x {S // 64} channels per batch; "
+                      f"{t_used:.1f} s of oracle time, fp64 sums, {threads} OpenMP threads)"}
+
+
+def stream_floor(torch, sp, bufs, steps, replays):
+    """Plain streaming read of the rotating buffers, one launch per buffer as
+    the layer does: GB/s and the average microseconds per buffer."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nbytes = bufs[0].numel() * bufs[0].element_size()
+
+    def record(n):
+        for i in range(n):
+            sp.spear_stream_read(bufs[i % len(bufs)], sink)
+    t = time_graph(torch, record, steps, replays)
+    return nbytes / (t["median"] * 1e-3) / 1e9, t["median"] * 1e3, nbytes
+
+
 def run_c2(args, torch, sp, gen):
     Ms = (1, 4, 8)
     d0 = gen.make(2, M=1)
@@ -174,11 +244,11 @@ def run_c2(args, torch, sp, gen):
     for M in Ms:
         assert wsp.numel() >= sp.spear_w4_linear_workspace_size(M, N, K, r)
 
-    def steps_fn(use_ec):
+    def steps_fn(use_ec, only=None):
         def record(n):
             for i in range(n):
                 c = i % R
-                for M in Ms:
+                for M in (Ms if only is None else (only,)):
                     sp.spear_w4_linear(xs[M], ws[c], ecs[c] if use_ec else None, y=ys[M],
                                        workspace=wsp, path=sp.PATH_AUTO)
         return record
@@ -186,9 +256,18 @@ def run_c2(args, torch, sp, gen):
     for i in range(args.warmup):
         steps_fn(True)(1)
     torch.cuda.synchronize()
-    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
-    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    t_ec = time_graph(torch, steps_fn(True), args.steps, args.replays)
+    t_plain = time_graph(torch, steps_fn(False), args.steps, args.replays)
+    per_m = {}
+    for M in Ms:
+        te = time_graph(torch, steps_fn(True, M), args.steps, args.replays)
+        tp = time_graph(torch, steps_fn(False, M), args.steps, args.replays)
+        per_m[str(M)] = {"fused_us": round(te["median"] * 1e3, 3),
+                         "plain_us": round(tp["median"] * 1e3, 3),
+                         "ec_overhead": round(te["median"] / tp["median"] - 1.0, 4)}
     assert sp.spear_workspace_timeouts(wsp) == 0
+    floor_gbs, floor_us, floor_bytes = stream_floor(torch, sp, [w.packed for w in ws],
+                                                    args.steps, args.replays)
 
     per_step_bytes = 0.0
     per_step_plain = 0.0
@@ -196,7 +275,7 @@ def run_c2(args, torch, sp, gen):
         w, ec, io = layer_bytes(M, N, K, r, True)
         per_step_bytes += w + ec + io
         per_step_plain += w + io
-    ms_step = t_ec / args.steps
+    ms_step = t_ec["median"]
     launches = len(Ms)
     achieved = (per_step_bytes / launches) / (ms_step / launches * 1e-3) / 1e9
     out = {
@@ -216,22 +295,35 @@ def run_c2(args, torch, sp, gen):
                                "asymmetric per-channel (bf16 scales, zero points 6..9), "
                                "bf16 activations N(0,1), EC rank 32 soft gate, fp32 output",
                    "rotating_weight_copies": R, "launches_per_step": launches,
-                   "timing": "HIP graph replay, HIP events on the launch stream"},
-        "ec_overhead": round(t_ec / t_plain - 1.0, 4),
-        "plain_ms_per_step": round(t_plain / args.steps, 6),
-        "plain_GBps": round(per_step_plain / (t_plain / args.steps * 1e-3) / 1e9, 2),
+                   "timing": f"median of {len(t_ec['all'])} replays of a {args.steps}-step "
+                             "HIP graph, HIP events on the launch stream"},
+        "timing": stats_ms(t_ec),
+        "ec_overhead": round(t_ec["median"] / t_plain["median"] - 1.0, 4),
+        "plain_ms_per_step": round(t_plain["median"], 6),
+        "plain_timing": stats_ms(t_plain),
+        "plain_GBps": round(per_step_plain / (t_plain["median"] * 1e-3) / 1e9, 2),
         "us_per_launch": round(ms_step / launches * 1e3, 3),
+        "per_M_launch": per_m,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(),
                      "traffic_unit": "bytes per launch (profiles/decode_fused_c2_hbm_traffic.md)",
                      "kernel": "decode_kernel<1,1,*,*> (fused EC, fp32 out)",
-                     "bytes_per_launch": round(per_step_bytes / launches)},
+                     "bytes_per_launch": round(per_step_bytes / launches),
+                     "stream_floor_GBps": round(floor_gbs, 2),
+                     "stream_floor_us_per_buffer": round(floor_us, 3),
+                     "stream_floor_buffer_bytes": floor_bytes,
+                     "frac_of_stream_floor": round(achieved / floor_gbs, 4),
+                     "plain_frac_of_stream_floor": round(
+                         (per_step_plain / launches) / (t_plain["median"] / launches * 1e-3)
+                         / 1e9 / floor_gbs, 4)},
     }
     return out
 
 
-def run_c4(args, torch, sp, gen):
+def measure_c4(args, torch, sp, gen, steps):
+    """C4 prefill: the layer with the EC and without, `steps` calls per graph
+    replay; -> dict of the measured quantities."""
     d = gen.make(4)
     M, N, K, r = d["M"], d["N"], d["K"], d["ec"]["r"]
     R = max(2, min(args.copies, 4))
@@ -250,13 +342,40 @@ def run_c4(args, torch, sp, gen):
     for _ in range(args.warmup):
         steps_fn(True)(1)
     torch.cuda.synchronize()
-    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
-    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    t_ec = time_graph(torch, steps_fn(True), steps, args.replays)
+    t_plain = time_graph(torch, steps_fn(False), steps, args.replays)
+    assert sp.spear_workspace_timeouts(wsp) == 0
     flops = 2.0 * M * N * K
     ec_flops = 2.0 * M * K * r + 2.0 * M * r * N
-    ms = t_ec / args.steps
-    tf = (flops + ec_flops) / (ms * 1e-3) / 1e12
-    tf_plain = flops / (t_plain / args.steps * 1e-3) / 1e12
+    return {"M": M, "N": N, "K": K, "r": r, "flops": flops, "ec_flops": ec_flops,
+            "t_ec": t_ec, "t_plain": t_plain}
+
+
+def prefill_object(args, torch, sp, gen):
+    m = measure_c4(args, torch, sp, gen, args.prefill_steps)
+    ms, ms0 = m["t_ec"]["median"], m["t_plain"]["median"]
+    tf = (m["flops"] + m["ec_flops"]) / (ms * 1e-3) / 1e12
+    tf0 = m["flops"] / (ms0 * 1e-3) / 1e12
+    out = {"workload": "C4 prefill: M=N=K=4096, int4 symmetric per-channel, Student-t(4) "
+                       "activations, EC rank 32 soft gate, fp32 output",
+           "unit": "TFLOP/s", "TFLOPs": round(tf, 2), "plain_TFLOPs": round(tf0, 2),
+           "ms_per_call": round(ms, 5), "plain_ms_per_call": round(ms0, 5),
+           "ec_overhead": round(ms / ms0 - 1.0, 4),
+           "timing": stats_ms(m["t_ec"], 5), "plain_timing": stats_ms(m["t_plain"], 5),
+           "roofline": {"bound": "mfma", "achieved": round(tf0, 2), "peak": BF16_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf0 / BF16_PEAK_TFLOPS, 4),
+                        "traffic": None,
+                        "kernel": "gemm2_kernel<2,4,0,0,1,1,4,4,1> (plain, 256 x 128 tiles, "
+                                  "whole K; one launch a call)",
+                        "flops_per_launch": m["flops"]}}
+    return out
+
+
+def run_c4(args, torch, sp, gen):
+    m = measure_c4(args, torch, sp, gen, args.steps)
+    ms, ms0 = m["t_ec"]["median"], m["t_plain"]["median"]
+    tf = (m["flops"] + m["ec_flops"]) / (ms * 1e-3) / 1e12
+    tf0 = m["flops"] / (ms0 * 1e-3) / 1e12
     return {
         "metric": METRIC, "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 6),
@@ -264,10 +383,12 @@ def run_c4(args, torch, sp, gen):
         "data": "synthetic",
         "config": {"workload": "C4 prefill: M=N=K=4096, int4 symmetric per-channel, "
                                "Student-t(4) activations, EC rank 32 soft gate, fp32 output"},
-        "ec_overhead": round(t_ec / t_plain - 1.0, 4),
-        "plain_TFLOPs": round(tf_plain, 2),
-        "roofline": {"bound": "mfma", "achieved": round(tf_plain, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf_plain / BF16_PEAK_TFLOPS, 4),
+        "timing": stats_ms(m["t_ec"]),
+        "ec_overhead": round(ms / ms0 - 1.0, 4),
+        "plain_TFLOPs": round(tf0, 2),
+        "plain_timing": stats_ms(m["t_plain"]),
+        "roofline": {"bound": "mfma", "achieved": round(tf0, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf0 / BF16_PEAK_TFLOPS, 4),
                      "traffic": None, "kernel": "gemm2_kernel<2,4,0,0,1,1,4,4,1> (plain, whole K)"},
     }
 
@@ -294,8 +415,8 @@ def run_c1(args, torch, sp, gen):
     for _ in range(args.warmup):
         steps_fn(True)(1)
     torch.cuda.synchronize()
-    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
-    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    t_ec = time_graph(torch, steps_fn(True), args.steps, args.replays)["median"] * args.steps
+    t_plain = time_graph(torch, steps_fn(False), args.steps, args.replays)["median"] * args.steps
     assert sp.spear_workspace_timeouts(wsp) == 0
     w, ecb, io = layer_bytes(M, N, K, r, False)
     ms = t_ec / args.steps
@@ -340,8 +461,8 @@ def run_c3(args, torch, sp, gen):
     for _ in range(args.warmup):
         steps_fn(True)(1)
     torch.cuda.synchronize()
-    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
-    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    t_ec = time_graph(torch, steps_fn(True), args.steps, args.replays)["median"] * args.steps
+    t_plain = time_graph(torch, steps_fn(False), args.steps, args.replays)["median"] * args.steps
     w, ecb, io = layer_bytes(M, N, K, r, True)
     ms = t_ec / args.steps
     gbs = (w + ecb + io) / (ms * 1e-3) / 1e9
@@ -401,8 +522,8 @@ def run_c5(args, torch, sp, gen):
     for _ in range(args.warmup):
         steps_fn(True)(1)
     torch.cuda.synchronize()
-    t_ec, _ = time_graph(torch, steps_fn(True), args.steps)
-    t_plain, _ = time_graph(torch, steps_fn(False), args.steps)
+    t_ec = time_graph(torch, steps_fn(True), args.steps, args.replays)["median"] * args.steps
+    t_plain = time_graph(torch, steps_fn(False), args.steps, args.replays)["median"] * args.steps
     assert sp.spear_workspace_timeouts(wsp) == 0
     byts = sum(sum(layer_bytes(M, N, K, r, True)) for (N, K, w, ec, r) in layers)
     flops = sum(2.0 * M * N * K + (2.0 * M * K * r + 2.0 * M * r * N if r else 0.0)
@@ -449,8 +570,12 @@ def main():
     out = run(args, torch, sp, gen)
     if args.copy_calibration:
         out["copy_calibration_bytes"] = copy_calibration(torch)
+    if args.workload == "c2" and not args.no_prefill:
+        out["prefill"] = prefill_object(args, torch, sp, gen)
     if args.workload == "c2" and not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline_c2((1, 4, 8), args.cpu_seconds)
+        if "prefill" in out:
+            out["prefill"]["cpu_baseline"] = cpu_baseline_c4(args.cpu_seconds)
     print(json.dumps(out), flush=True)
 
 

@@ -34,14 +34,22 @@
  * Conventions shared by every entry point:
  *   - Data pointers are DEVICE pointers unless stated otherwise.  The caller
  *     allocates and owns all memory, including the workspace.  The library
- *     never allocates device memory and keeps no per-call state.
+ *     never allocates device memory.
+ *   - State: the workspace carries state from call to call (launch counters
+ *     and tagged partial results, see spear_workspace_init), so it is zeroed
+ *     once and then left to the library.  The only other state is the
+ *     process-wide wait limit (spear_set_wait_limit) and a per-device cache of
+ *     the gfx950 check.
  *   - Every call enqueues work on `stream` (a hipStream_t; NULL is the null
  *     stream) and returns without synchronising.  Faults inside a kernel
  *     surface at the caller's next synchronisation.
- *   - Arguments are validated on the host before any HIP call.  A call that
- *     returns an error has enqueued nothing.
- *   - All functions are thread-safe.  A workspace must not be shared by calls
- *     that may run concurrently (for example on two streams).
+ *   - Arguments are validated on the host before any HIP call; a call that
+ *     fails validation has enqueued nothing.  A call that makes several
+ *     launches and returns SPEAR_E_HIP may have enqueued the launches before
+ *     the one that failed; the outputs are then unspecified.
+ *   - Entry points may be called from several threads at once.  A workspace
+ *     must not be shared by calls that may run concurrently (for example on
+ *     two streams).
  */
 #ifndef SPEAR_H
 #define SPEAR_H
@@ -196,18 +204,34 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
                                   void *stream);
 
 /*
- * Some launches wait (bounded) for EC values that other workgroups of the same
- * launch produce: the fused decode kernel's epilogue, the split pre-pass's last
- * slice and, on the K-split prefill path, the GEMM epilogue.  If a wait exceeds
- * the limit the outputs it covers (a decode workgroup's channels, a pre-pass
- * token group, a GEMM tile) are written without the EC and a counter in the
- * workspace is incremented.  spear_set_wait_limit sets the limit in polling
- * rounds for later launches (0 restores the default, about a second);
+ * Some launches wait (bounded) for values that other workgroups of the same
+ * launch produce: the fused decode kernel's epilogue (the EC partials), the
+ * decode kernel's last K range (the other ranges' sums), the split pre-pass's
+ * last slice and, where the pre-pass shares the GEMM's launch, the GEMM
+ * epilogue.  If a wait exceeds the limit, every output whose sum it leaves
+ * incomplete is written as NaN -- a decode workgroup's channels for all
+ * tokens, a pre-pass token group's rows, a GEMM tile -- the affected g_out
+ * entries are NaN, *n_active_out is -1, and a counter in the workspace is
+ * incremented.  No expired wait ever yields a finite but wrong output.
+ * spear_set_wait_limit sets the limit in polling rounds for launches enqueued
+ * afterwards, from any thread (0 restores the default, about a second);
  * spear_workspace_timeouts synchronises `stream`, copies the counter to
  * *host_count and clears it.
  */
 void spear_set_wait_limit(uint32_t rounds);
 spear_status spear_workspace_timeouts(void *workspace, int32_t *host_count, void *stream);
+
+/*
+ * spear_stream_read -- measurement helper, not part of the layer: reads every
+ * byte of buf once (16-byte loads, four a thread in flight) and writes
+ * nothing to *sink in practice (it is written only if the XOR of the data
+ * equals a fixed constant, so that the loads cannot be optimised away).  Its
+ * rate is the plain read floor that the decode kernel's bandwidth is compared
+ * with, for buffers of the layer's size.
+ *   buf  device pointer, 16-byte aligned; bytes >= 16 and a multiple of 16.
+ *   sink device pointer to one uint32, 4-byte aligned.
+ */
+spear_status spear_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 const char *spear_status_string(spear_status s);
 int32_t spear_abi_version(void);

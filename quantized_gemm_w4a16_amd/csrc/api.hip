@@ -5,6 +5,7 @@
 // Error-Adaptive Recovery Enabling Efficient Low-Bit LLM Serving",
 // gist.science summary section 2.2 A (decode: EC fused into the low-bit GEMM
 // epilogue; prefill: EC semi-fused).
+#include <atomic>
 #include <math.h>
 #include <mutex>
 #include <string.h>
@@ -158,7 +159,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
     return L;
 }
 
-static uint32_t g_wait_limit = 0;
+// Wait limit of later launches (0: the default); set from any thread.
+static std::atomic<uint32_t> g_wait_limit{0};
 static const uint32_t DEFAULT_WAIT_LIMIT = 1u << 20;
 
 // gfx950 check, cached per device.
@@ -220,7 +222,21 @@ const char *spear_status_string(spear_status s)
     }
 }
 
-void spear_set_wait_limit(uint32_t rounds) { g_wait_limit = rounds; }
+void spear_set_wait_limit(uint32_t rounds) { g_wait_limit.store(rounds, std::memory_order_relaxed); }
+
+spear_status spear_stream_read(const void *buf, size_t bytes, uint32_t *sink, void *stream)
+{
+    if (!buf || !sink)
+        return SPEAR_E_NULL;
+    if (bytes < 16 || bytes % 16 != 0)
+        return SPEAR_E_SHAPE;
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return SPEAR_E_ALIGN;
+    spear_status st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    return hip_status(launch_stream_read(buf, bytes, sink, (hipStream_t)stream));
+}
 
 spear_status spear_pack_w4(const void *codes, int32_t code_kind, int64_t N, int64_t K,
                            uint8_t *packed, int32_t *bad_codes, void *stream)
@@ -388,7 +404,8 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
     a.g_ks = gemm_ks(M, N, K, path == SPEAR_PATH_PREFILL_LARGE);
     a.L = L;
     a.out_f32 = out_dtype == SPEAR_OUT_F32;
-    a.wait_limit = g_wait_limit ? g_wait_limit : DEFAULT_WAIT_LIMIT;
+    const uint32_t wl = g_wait_limit.load(std::memory_order_relaxed);
+    a.wait_limit = wl ? wl : DEFAULT_WAIT_LIMIT;
     if (ec) {
         a.A = ec->A;
         a.B = ec->B;

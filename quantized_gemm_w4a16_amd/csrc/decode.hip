@@ -264,7 +264,7 @@ __device__ void ec_produce_gv(const LinearArgs &a, int64_t p, int wave, int lane
 // on the vector ALU in fp32: lane (c, g) forms the partial of channel c over
 // ranks 8 g .. 8 g + 7, the four partials meet by shuffles in order, and each
 // lane then picks its four output channels.  Returns, in wave 0, e[i] for
-// channel 16 cg + 4 lg + i and token lr; *ok_out is false (and the term zero)
+// channel 16 cg + 4 lg + i and token lr; *ok_out is false (and the term NaN)
 // when a bounded wait expired.  Writes the gate outputs when cg == 0.
 template <int KM, int GV, typename F>
 __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, int wave, int lane,
@@ -462,7 +462,20 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
     // the gate of the lane's token (token 0 with one token)
     const float gs = GV ? (__shfl(act, 0) ? __shfl(g, 0) : 0.f) : (act ? g : 0.f);
     *ok_out = ok;
-    return ok ? e * gs : f32x4{0.f, 0.f, 0.f, 0.f};
+    if (!ok) {
+        // An expired wait: the EC term of every token of this channel group is
+        // unknown, so its outputs become NaN; the first channel group also
+        // marks the gate outputs (g NaN, n_active -1).
+        const float qnan = __builtin_nanf("");
+        if (cg == 0 && wave == 0) {
+            if (lane < M && a.g_out)
+                a.g_out[lane] = qnan;
+            if (lane == 0 && a.nact_out)
+                *a.nact_out = -1;
+        }
+        return f32x4{qnan, qnan, qnan, qnan};
+    }
+    return e * gs;
 }
 
 template <int EC_MODE, int OUT_F32, int SW, int GV>
@@ -705,7 +718,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
         //    device-coherent stores) and leaves; the channel group's last range
         //    -- its highest block index, dispatched after the others, which never
         //    wait -- re-loads them until every tag is this launch's (bounded; an
-        //    expired wait is counted and leaves the missing ranges out), adds
+        //    expired wait is counted and makes the channels' outputs NaN), adds
         //    them in range order and then its own.  No fence: a release fence
         //    per workgroup would write back the whole L2 (measured: 20 against
         //    8.7 us for M = 16, K = 8192).
@@ -766,6 +779,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
                     }
                     tot = st + tot;
                     rst = sr + rst;
+                    if (!ok) {
+                        // an expired wait: these channels' sums are incomplete
+                        const float qnan = __builtin_nanf("");
+                        tot = f32x4{qnan, qnan, qnan, qnan};
+                        rst = qnan;
+                    }
                 }
             }
         }

@@ -104,16 +104,25 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t *__restrict__ 
 // One workgroup of 1024 threads walks the tokens in chunks of 1024.  flags may
 // alias idx: a chunk's flags are all read before any of its indices is written,
 // and every write lands below the next chunk.  idx may be NULL (count only).
+// A negative flag marks a token whose gate is unknown (an expired wait
+// upstream); the count is then -1.
 __global__ __launch_bounds__(1024) void compact_kernel(const int32_t *flags, int64_t M,
                                                        int32_t *idx, int32_t *nact)
 {
     __shared__ int wave_tot[16];
+    __shared__ int any_bad;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    if (tid == 0)
+        any_bad = 0;
+    __syncthreads();
     int64_t base = 0;
     for (int64_t c0 = 0; c0 < M; c0 += 1024) {
         const int64_t i = c0 + tid;
-        const int f = (i < M) ? (flags[i] != 0) : 0;
+        const int32_t fv = (i < M) ? flags[i] : 0;
+        const int f = fv != 0;
         const uint64_t mask = __ballot(f);
+        if (fv < 0)
+            any_bad = 1;
         if (lane == 0)
             wave_tot[wave] = __popcll(mask);
         __syncthreads();
@@ -130,7 +139,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const int32_t *flags, int
         __syncthreads();
     }
     if (tid == 0 && nact)
-        *nact = (int32_t)base;
+        *nact = any_bad ? -1 : (int32_t)base;
 }
 
 hipError_t launch_gate(const uint16_t *x, int64_t M, int64_t K, const uint16_t *wg, float b,
@@ -174,6 +183,42 @@ hipError_t launch_zero(void *p, size_t bytes, hipStream_t s)
     if (blocks > 4096)
         blocks = 4096;
     hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint8_t *)p, bytes);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ stream read
+// Measurement helper: every 16-byte chunk of p is loaded once, four loads a
+// thread in flight, and folded by XOR; the fold is stored only if it equals a
+// constant, so the loads cannot be removed and (almost surely) nothing is
+// written.  Its rate is the plain read floor of a buffer of that size.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4 *__restrict__ p, size_t n16,
+                                                          uint32_t *sink)
+{
+    const size_t stride = (size_t)gridDim.x * 256;
+    uint32_t acc = 0;
+    for (size_t base = (size_t)blockIdx.x * 256 + threadIdx.x; base < n16; base += 4 * stride) {
+        u32x4 v[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const size_t i = base + j * stride;
+            v[j] = i < n16 ? p[i] : zero4();
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    }
+    if (acc == 0x9E3779B9u)
+        *sink = acc;
+}
+
+hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, hipStream_t s)
+{
+    const size_t n16 = bytes / 16;
+    size_t blocks = (n16 + 1023) / 1024;
+    if (blocks > 4096)
+        blocks = 4096;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       reinterpret_cast<const u32x4 *>(p), n16, sink);
     return hipGetLastError();
 }
 

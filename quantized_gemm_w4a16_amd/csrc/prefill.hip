@@ -26,8 +26,9 @@ namespace {
 // as tagged words {value, launch epoch} (relaxed device-coherent stores), and
 // the last slice -- the group's highest block index, dispatched after the
 // others, which never wait -- re-loads the other slices' words until every tag
-// is this launch's (bounded; an expired wait drops the group's EC term and is
-// counted), adds the slices in order and finishes the tokens.  Each word is
+// is this launch's (bounded; an expired wait is counted and makes the group's
+// v, g and selection flags NaN / -1, so that its outputs come out NaN), adds
+// the slices in order and finishes the tokens.  Each word is
 // validated on its own, so no fence or counter is involved (a release fence
 // per workgroup would write back the whole L2).
 //
@@ -61,10 +62,11 @@ struct PreShared {
 // sums (without b) in s_zw and u in s_uw (tile t, lane l: ranks 16 t + 4 (l / 16)
 // + i of token l % 16): gate, selection, v = g u as bf16 hi + lo.  Called by
 // every thread of the workgroup; waves below nwaves write v (as tagged words
-// when tagged).
+// when tagged).  bad (an expired wait upstream): the group's sums are
+// incomplete, so g and v are NaN and each real token's selection flag is -1.
 __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_uw)[64],
                                const double *s_zw, float *s_g, int *s_act, int tid, int lane,
-                               int wave, int nwaves, bool tagged, uint32_t tag)
+                               int wave, int nwaves, bool tagged, uint32_t tag, bool bad)
 {
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, m = m0 + lr;
@@ -76,8 +78,8 @@ __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_
     if (tid < 16) {
         const double z = (double)a.b + s_zw[tid];
         const int64_t mm = m0 + tid;
-        const float g = (float)(1.0 / (1.0 + exp(-z)));
-        const int act = (mm < M) && (a.hard ? (z > a.thr) : 1);
+        const float g = bad ? __builtin_nanf("") : (float)(1.0 / (1.0 + exp(-z)));
+        const int act = bad ? (mm < M ? -1 : 0) : (mm < M) && (a.hard ? (z > a.thr) : 1);
         s_g[tid] = g;
         s_act[tid] = act;
         active[mm] = act;
@@ -217,6 +219,7 @@ __device__ __forceinline__ void prepass_tail(const LinearArgs &a, const int64_t 
     const int64_t KS = a.pre_ks, m0 = grp * 16;
     const int ntile = a.rpad / 16;
     uint32_t tag = 0;
+    bool bad = false;
     if (KS > 1 || tagged) {
         if (tid == 0) {
             *sh.tag = epoch_tag(claimed + opaque_zero64());
@@ -329,18 +332,11 @@ __device__ __forceinline__ void prepass_tail(const LinearArgs &a, const int64_t 
         if (!ok)
             atomicOr(sh.bad, 1u);
         __syncthreads();
-        if (*sh.bad) {
-            // an expired wait: the group takes no EC term (g = 0, not selected)
-            if (tid == 0)
-                atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
-            if (tid < 16)
-                sh.zw[tid] = -INFINITY;
-            for (int e = tid; e < nel; e += 64 * PW)
-                uwm[e] = 0.f;
-            __syncthreads();
-        }
+        bad = *sh.bad != 0;
+        if (bad && tid == 0)          // an expired wait: counted; the group's v is NaN
+            atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
     }
-    prepass_finish(a, m0, sh.uw, sh.zw, sh.g, sh.act, tid, lane, wave, PW, tagged, tag);
+    prepass_finish(a, m0, sh.uw, sh.zw, sh.g, sh.act, tid, lane, wave, PW, tagged, tag, bad);
 }
 
 __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArgs a)
@@ -1013,8 +1009,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
         // after the main loop) until every tag is this launch's; when they are
         // not all there at the first try, a wave polls one word (one request)
         // before it reloads, so that early tiles do not flood the memory system
-        // the pre-pass needs.  Bounded; an expired wait drops this chunk's EC
-        // term for the whole tile and is counted.
+        // the pre-pass needs.  Bounded; an expired wait makes the whole tile
+        // NaN (its EC term is unknown) and is counted.
         const uint64_t *vtag = reinterpret_cast<const uint64_t *>(a.ws + a.L.vtag);
         const uint32_t tag = s_tagg;
         const int rpad = a.rpad, r = a.r;
@@ -1070,6 +1066,12 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
             if (s_tbad & (1u << (t & 31))) {
                 if (tid == 0)
                     atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+                const float qnan = __builtin_nanf("");
+#pragma unroll
+                for (int fn = 0; fn < G2_FN; fn++)
+#pragma unroll
+                    for (int fm = 0; fm < G2_FM; fm++)
+                        acc[fn][fm] = f32x4{qnan, qnan, qnan, qnan};
                 __syncthreads();                                      // s_v is rewritten next
                 continue;
             }

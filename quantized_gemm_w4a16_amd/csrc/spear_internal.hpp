@@ -263,6 +263,7 @@ hipError_t launch_gate(const uint16_t *x, int64_t M, int64_t K, const uint16_t *
 hipError_t launch_compact(const int32_t *flags, int64_t M, int32_t *idx, int32_t *nact,
                           hipStream_t s);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_decode(const LinearArgs &a, int ec_mode, hipStream_t s);
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s);
 hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStream_t s);

@@ -31,8 +31,8 @@ MAX_RANK = 256
 
 EXPORTS = ("spear_pack_w4", "spear_gate", "spear_w4_linear_workspace_size",
            "spear_workspace_init", "spear_w4_linear", "spear_w4_linear_path",
-           "spear_set_wait_limit", "spear_workspace_timeouts", "spear_status_string",
-           "spear_abi_version")
+           "spear_set_wait_limit", "spear_workspace_timeouts", "spear_stream_read",
+           "spear_status_string", "spear_abi_version")
 
 
 class SpearError(RuntimeError):
@@ -77,11 +77,12 @@ def load():
     lib.spear_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.spear_set_wait_limit.restype = None
     lib.spear_workspace_timeouts.argtypes = [P, ctypes.POINTER(i32), P]
+    lib.spear_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
     lib.spear_status_string.argtypes = [i32]
     lib.spear_status_string.restype = ctypes.c_char_p
     lib.spear_abi_version.restype = i32
     for name in ("spear_pack_w4", "spear_gate", "spear_workspace_init", "spear_w4_linear",
-                 "spear_w4_linear_path", "spear_workspace_timeouts"):
+                 "spear_w4_linear_path", "spear_workspace_timeouts", "spear_stream_read"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -216,3 +217,11 @@ def spear_workspace_timeouts(ws: torch.Tensor, stream=None) -> int:
     _check("spear_workspace_timeouts", load().spear_workspace_timeouts(_ptr(ws), ctypes.byref(out),
                                                                        _stream(stream)))
     return int(out.value)
+
+
+def spear_stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None,
+                      stream=None):
+    """Measurement helper: read every byte of buf once (the plain read floor)."""
+    n = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    _check("spear_stream_read", load().spear_stream_read(_ptr(buf), n, _ptr(sink),
+                                                         _stream(stream)))

@@ -271,26 +271,51 @@ def test_workspace_reuse_across_calls():
     assert np.all(ctr == np.uint64(len(shapes) << 32)), ctr
 
 
+def nan_or_exact(y, full, n, blocks, what):
+    """After a forced short wait: every output is NaN or equal to the full
+    result, NaN comes in whole blocks (each NaN element lies in some fully NaN
+    block of one of the listed (rows, cols) shapes), and some wait expired
+    (n > 0) exactly when some output is NaN."""
+    nan = np.isnan(y)
+    ok = nan | np.isclose(y, full, rtol=0, atol=1e-5)
+    assert np.all(ok), what
+    M, N = y.shape
+    for (m, c) in zip(*np.nonzero(nan)):
+        covered = False
+        for (br, bc) in blocks:
+            r0, c0 = (m // br) * br, (c // bc) * bc
+            if np.all(nan[r0:min(r0 + br, M), c0:min(c0 + bc, N)]):
+                covered = True
+                break
+        assert covered, (what, m, c)
+    print(f"[timeout] {what}: expired waits {n}, NaN outputs {int(nan.sum())}", flush=True)
+    assert (n > 0) == bool(nan.any()), (what, n, int(nan.sum()))
+
+
 def test_forced_wait_timeout_is_reported():
-    """A zero wait limit makes the fused epilogues give up at once: the call still
-    completes, each output is the plain or the compensated value, and the
-    expired waits are counted."""
+    """A wait limit of one poll makes the fused decode epilogues give up early:
+    the call still completes, each 16-channel group's outputs are either exact
+    or NaN for every token (never a finite wrong value), the expired waits are
+    counted, n_active is -1 when the first group gave up, and the next call with
+    the default limit is exact again."""
     d = random_case(4, 4096, 4096, 32, oracle.CODES_U4, 0, seed=9)
     w = gpu_weights(d)
     ws = sp.new_workspace(4, 4096, 4096, 32)
-    plain, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ec=False)
-    full, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
+    full, e = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
     assert sp.spear_workspace_timeouts(ws) == 0
+    assert_close(full, run_oracle(d), "fused decode before the forced timeouts")
     try:
         sp.spear_set_wait_limit(1)
-        y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
+        y, e = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
         n = sp.spear_workspace_timeouts(ws)
     finally:
         sp.spear_set_wait_limit(0)
-    ok = np.isclose(y, plain, rtol=0, atol=1e-6) | np.isclose(y, full, rtol=0, atol=1e-6)
-    assert np.all(ok)
-    print(f"[timeout] expired waits: {n}")
-    assert n >= 0
+    nan_or_exact(y, full, n, [(4, 16)], "fused decode")
+    nact = int(e.n_active_out.item())
+    assert nact in (-1, 4)
+    if nact == -1:
+        assert np.all(np.isnan(y[:, :16]))
+        assert np.all(np.isnan(host(e.g_out)))
     y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws)
     assert np.array_equal(y, full)
 
@@ -298,8 +323,8 @@ def test_forced_wait_timeout_is_reported():
 def test_decode_ksplit_wait_timeout_is_reported():
     """Decode with K split over workgroups: the channel group's last range waits,
     bounded, for the other ranges' tagged sums.  With a wait limit of one poll it
-    may give up (the expiry is counted; the missing ranges are left out of those
-    channels); with the default limit the next call is exact."""
+    may give up: those channels are then NaN for every token and the expiry is
+    counted; with the default limit the next call is exact."""
     d = random_case(16, 512, 8192, 32, oracle.CODES_U4, 0, seed=23)
     w = gpu_weights(d)
     ws = sp.new_workspace(16, 512, 8192, 32)
@@ -312,39 +337,39 @@ def test_decode_ksplit_wait_timeout_is_reported():
         n = sp.spear_workspace_timeouts(ws)
     finally:
         sp.spear_set_wait_limit(0)
-    print(f"[timeout] expired K-range waits: {n}")
-    assert n > 0 or np.array_equal(y, full)
+    nan_or_exact(y, full, n, [(16, 16)], "decode K split")
     y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ws=ws, ec=False)
     assert np.array_equal(y, full)
 
 
-def test_prepass_wait_timeout_drops_group_ec():
+@pytest.mark.parametrize("r", [32, 64])
+def test_prepass_wait_timeout_gives_nan(r):
     """The split pre-pass's finisher waits, bounded, for the other slices' tagged
-    words, and here (a K-split GEMM) the GEMM epilogues wait the same way for
-    the pre-pass blocks' tagged v.  With a wait limit of one poll either may give
-    up: the tokens it covers then take no EC term in the channels it covers
-    (each 256-channel block of an output row is the plain or the compensated
-    one), the expiry is counted, and the next call with the default limit is
-    exact."""
-    d = random_case(32, 512, 4096, 32, oracle.CODES_U4, 0, seed=19)
+    words, and here (the pre-pass in the GEMM's launch) the GEMM epilogues wait
+    the same way for the pre-pass blocks' tagged v.  With a wait limit of one
+    poll either may give up: a 16-token group's rows (pre-pass) or a 64 x 64
+    tile (epilogue) are then NaN, n_active is -1 if the gate is incomplete, the
+    expiry is counted, and the next call with the default limit is exact."""
+    d = random_case(32, 512, 4096, r, oracle.CODES_U4, 0, seed=19 + r)
     w = gpu_weights(d)
-    ws = sp.new_workspace(32, 512, 4096, 32)
-    plain, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ec=False)
+    ws = sp.new_workspace(32, 512, 4096, r)
     full, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
-    assert_close(full, run_oracle(d), "split pre-pass")
+    assert_close(full, run_oracle(d), f"split pre-pass r={r}")
     assert sp.spear_workspace_timeouts(ws) == 0
     try:
         sp.spear_set_wait_limit(1)
-        y, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
+        y, e = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
         n = sp.spear_workspace_timeouts(ws)
     finally:
         sp.spear_set_wait_limit(0)
-    for m in range(d["M"]):
-        for c in range(0, d["N"], 256):
-            blk = slice(c, c + 256)
-            assert (np.allclose(y[m, blk], plain[m, blk], rtol=0, atol=1e-5) or
-                    np.allclose(y[m, blk], full[m, blk], rtol=0, atol=1e-5)), (m, c)
-    print(f"[timeout] expired waits: {n}")
+    nan_or_exact(y, full, n, [(16, 512), (64, 64)], f"prefill r={r}")
+    nact = int(e.n_active_out.item())
+    assert nact in (-1, 32)
+    gnan = np.isnan(host(e.g_out))
+    assert (nact == -1) == bool(gnan.any())
+    for g0 in range(0, 32, 16):
+        if gnan[g0:g0 + 16].any():
+            assert np.all(gnan[g0:g0 + 16]) and np.all(np.isnan(y[g0:g0 + 16]))
     y, _ = run_gpu(d, path=sp.PATH_PREFILL, w=w, ws=ws)
     assert np.array_equal(y, full)
 
