@@ -203,6 +203,32 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
                                   void *workspace, size_t ws_bytes, int32_t path,
                                   void *stream);
 
+/* Size of the library's own scratch used by spear_w4_linear_noalloc, per GPU. */
+#define SPEAR_NOALLOC_MAX_WORKSPACE ((size_t)48 << 20)
+
+/*
+ * spear_w4_linear_noalloc -- spear_w4_linear_path without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  The
+ * kernels are those of spear_w4_linear_path; the workspace they need is a
+ * file-scope device array of SPEAR_NOALLOC_MAX_WORKSPACE bytes inside the
+ * library (one per GPU, zero when the library is loaded, held until the
+ * process ends).  The call itself allocates nothing: no hipMalloc, no
+ * hipFree, no allocating library routine.
+ *   Arguments as for spear_w4_linear_path.  A layer whose workspace need
+ *   (spear_w4_linear_workspace_size) exceeds SPEAR_NOALLOC_MAX_WORKSPACE is
+ *   rejected with SPEAR_E_WORKSPACE before any HIP call.
+ * Every call on one GPU uses that GPU's single scratch array, which carries
+ * state from call to call (launch counters, tagged partials): calls that may
+ * overlap on one GPU (two streams, two threads) race and must not be made.
+ * Expired-wait counts of these calls stay inside the scratch (they are not
+ * readable through spear_workspace_timeouts); the NaN outputs described below
+ * still mark them.
+ */
+spear_status spear_w4_linear_noalloc(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                     const spear_ec *ec, void *y, int32_t out_dtype,
+                                     int32_t path, void *stream);
+
 /*
  * Some launches wait (bounded) for values that other workgroups of the same
  * launch produce: the fused decode kernel's epilogue (the EC partials), the

@@ -320,11 +320,17 @@ spear_status spear_workspace_timeouts(void *workspace, int32_t *host_count, void
     return SPEAR_OK;
 }
 
-spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4 *w,
-                                  const spear_ec *ec, void *y, int32_t out_dtype,
-                                  void *workspace, size_t ws_bytes, int32_t path, void *stream)
+} // extern "C"
+
+namespace spear {
+
+// Host-only argument checks of a layer call (no HIP call); *path is resolved
+// from SPEAR_PATH_AUTO.
+static spear_status validate_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                    const spear_ec *ec, const void *y, int32_t out_dtype,
+                                    const void *workspace, size_t ws_bytes, int32_t *path_io)
 {
-    // ---- validation (no HIP call before it passes)
+    int32_t path = *path_io;
     if (!w || !workspace || !w->packed || !w->scales)
         return SPEAR_E_NULL;
     if (M > 0 && (!x || !y))
@@ -359,6 +365,17 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
         return SPEAR_E_WORKSPACE;
     if (L.ncg * L.ksplit > GRID_MAX || cdiv(N, 64) * cdiv(M, 64) > GRID_MAX)
         return SPEAR_E_SHAPE;
+    *path_io = path;
+    return SPEAR_OK;
+}
+
+// A validated layer call: dispatch and launch on `stream`.
+static spear_status run_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                               const spear_ec *ec, void *y, int32_t out_dtype, void *workspace,
+                               int32_t path, void *stream)
+{
+    const int64_t N = w->N, K = w->K;
+    const WsLayout L = ws_layout(M, N, K, ec ? ec->r : 0);
     spear_status st = check_device();
     if (st != SPEAR_OK)
         return st;
@@ -465,6 +482,63 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
         break;
     }
     return hip_status(e);
+}
+
+// Scratch of the allocation-free entry point: one copy per GPU, zero at load
+// (static storage), held until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory; its device address is
+// looked up once per device and kept in scratch_ptr.
+static __device__ __align__(256) uint8_t scratch[SPEAR_NOALLOC_MAX_WORKSPACE];
+
+static spear_status scratch_address(void **out)
+{
+    static std::mutex mu;
+    static void *scratch_ptr[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return SPEAR_E_HIP;
+    if (dev < 0 || dev >= 64)
+        return SPEAR_E_DEVICE;
+    std::lock_guard<std::mutex> lk(mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return SPEAR_E_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return SPEAR_OK;
+}
+
+} // namespace spear
+
+extern "C" {
+
+spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                  const spear_ec *ec, void *y, int32_t out_dtype,
+                                  void *workspace, size_t ws_bytes, int32_t path, void *stream)
+{
+    spear_status st = validate_linear(x, M, w, ec, y, out_dtype, workspace, ws_bytes, &path);
+    if (st != SPEAR_OK)
+        return st;
+    return run_linear(x, M, w, ec, y, out_dtype, workspace, path, stream);
+}
+
+spear_status spear_w4_linear_noalloc(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                     const spear_ec *ec, void *y, int32_t out_dtype,
+                                     int32_t path, void *stream)
+{
+    // validated against the scratch's size with an aligned stand-in address
+    const void *standin = reinterpret_cast<const void *>((uintptr_t)256);
+    spear_status st = validate_linear(x, M, w, ec, y, out_dtype, standin,
+                                      SPEAR_NOALLOC_MAX_WORKSPACE, &path);
+    if (st != SPEAR_OK)
+        return st;
+    void *ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != SPEAR_OK)
+        return st;
+    return run_linear(x, M, w, ec, y, out_dtype, ws, path, stream);
 }
 
 spear_status spear_w4_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,

@@ -31,6 +31,7 @@ MAX_RANK = 256
 
 EXPORTS = ("spear_pack_w4", "spear_gate", "spear_w4_linear_workspace_size",
            "spear_workspace_init", "spear_w4_linear", "spear_w4_linear_path",
+           "spear_w4_linear_noalloc",
            "spear_set_wait_limit", "spear_workspace_timeouts", "spear_stream_read",
            "spear_status_string", "spear_abi_version")
 
@@ -74,6 +75,8 @@ def load():
     lin = [P, i64, ctypes.POINTER(_W4), ctypes.POINTER(_EC), P, i32, P, ctypes.c_size_t]
     lib.spear_w4_linear.argtypes = lin + [P]
     lib.spear_w4_linear_path.argtypes = lin + [i32, P]
+    lib.spear_w4_linear_noalloc.argtypes = [P, i64, ctypes.POINTER(_W4), ctypes.POINTER(_EC), P,
+                                            i32, i32, P]
     lib.spear_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.spear_set_wait_limit.restype = None
     lib.spear_workspace_timeouts.argtypes = [P, ctypes.POINTER(i32), P]
@@ -82,7 +85,8 @@ def load():
     lib.spear_status_string.restype = ctypes.c_char_p
     lib.spear_abi_version.restype = i32
     for name in ("spear_pack_w4", "spear_gate", "spear_workspace_init", "spear_w4_linear",
-                 "spear_w4_linear_path", "spear_workspace_timeouts", "spear_stream_read"):
+                 "spear_w4_linear_path", "spear_w4_linear_noalloc", "spear_workspace_timeouts",
+                 "spear_stream_read"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -205,6 +209,28 @@ def spear_w4_linear(x: torch.Tensor, w: W4, ec: Optional[EC] = None,
                                      _ptr(y), out_dtype, _ptr(workspace), workspace.numel(),
                                      path, _stream(stream))
     _check("spear_w4_linear", st)
+    return y
+
+
+NOALLOC_MAX_WORKSPACE = 48 << 20
+
+
+def spear_w4_linear_noalloc(x: torch.Tensor, w: W4, ec: Optional[EC] = None,
+                            y: Optional[torch.Tensor] = None, out_dtype: int = OUT_F32,
+                            path: int = PATH_AUTO, stream=None) -> torch.Tensor:
+    """The layer through the allocation-free entry point (the library's own
+    scratch stands in for the workspace).  y must be given by callers that
+    cannot allocate; it is allocated here only for convenience when None."""
+    M = int(x.shape[0])
+    if y is None:
+        dt = torch.float32 if out_dtype == OUT_F32 else torch.bfloat16
+        y = torch.empty((M, w.N), dtype=dt, device=x.device)
+    wc = w._c()
+    ecc = ec._c() if ec is not None else None
+    st = load().spear_w4_linear_noalloc(_ptr(x), M, ctypes.byref(wc),
+                                        ctypes.byref(ecc) if ecc is not None else None,
+                                        _ptr(y), out_dtype, path, _stream(stream))
+    _check("spear_w4_linear_noalloc", st)
     return y
 
 
