@@ -55,7 +55,7 @@ def _load():
                                 P, P, P, P]
     lib.oracle_gate.restype = None
     lin = [P, i64, i64, i64, P, P, P, ctypes.c_int, P, P, i64, P,
-           ctypes.c_float, ctypes.c_float, ctypes.c_int]
+           ctypes.c_float, ctypes.c_float, ctypes.c_int, i64, P, P, P, P, ctypes.c_float]
     lib.oracle_w4_linear.argtypes = lin + [P]
     lib.oracle_w4_linear.restype = ctypes.c_int
     lib.oracle_w4_linear_sampled.argtypes = lin + [i64, P, P, P]
@@ -126,7 +126,7 @@ def _lin_args(x, packed, scales, zeros, ec):
     assert packed.shape[1] * 2 == K
     keep = [x, packed, _c(scales, np.float32), _c(zeros, np.uint8)]
     if ec is None:
-        ecargs = [0, None, None, 0, None, 0.0, 0.0, 0]
+        ecargs = [0, None, None, 0, None, 0.0, 0.0, 0, 0, None, None, None, None, 1.0]
     else:
         A = _c(ec["A"], np.uint16)
         B = _c(ec["B"], np.uint16)
@@ -136,13 +136,27 @@ def _lin_args(x, packed, scales, zeros, ec):
         keep += [A, B, wg]
         ecargs = [1, _ptr(A), _ptr(B), r, _ptr(wg), float(ec["b"]), float(ec["tau"]),
                   int(ec["hard"])]
+        h = int(ec.get("gate_h", 0) or 0)
+        if h:
+            W1 = _c(ec["gate_w1"], np.float32)
+            c1 = _c(ec["gate_c1"], np.float32)
+            W2 = _c(ec["gate_w2"], np.float32)
+            c2 = _c(ec["gate_c2"], np.float32)
+            assert W1.shape == (h, r) and c1.shape == (h,) and W2.shape == (r, h)
+            assert c2.shape == (r,)
+            keep += [W1, c1, W2, c2]
+            ecargs += [h, _ptr(W1), _ptr(c1), _ptr(W2), _ptr(c2), float(ec.get("alpha", 1.0))]
+        else:
+            ecargs += [0, None, None, None, None, 1.0]
     args = [_ptr(keep[0]), M, K, N, _ptr(keep[1]), _ptr(keep[2]), _ptr(keep[3])] + ecargs
     return args, keep, M, N
 
 
 def w4_linear(x_bits, packed, scales, zeros=None, ec=None) -> np.ndarray:
     """Full layer output y [M][N] in fp64.  ec: dict(A [r][K] bf16 bits, B [N][r] bf16 bits,
-    w_g [K] bf16 bits, b, tau, hard) or None for the plain W4 linear."""
+    w_g [K] bf16 bits, b, tau, hard) or None for the plain W4 linear.  Optional vector
+    gate in ec: gate_h (hidden width, 0 = none), gate_w1 [h][r], gate_c1 [h],
+    gate_w2 [r][h], gate_c2 [r] (fp32) and alpha."""
     args, keep, M, N = _lin_args(x_bits, packed, scales, zeros, ec)
     y = np.empty((M, N), dtype=np.float64)
     rc = _load().oracle_w4_linear(*args, _ptr(y))

@@ -27,6 +27,13 @@
  *     alpha is folded into B (alpha = 1).
  *   - Hard gate: a token takes the EC iff its logit z_m > logit(tau); a tie
  *     skips.  Soft gate: every token takes it.
+ *   - Vector gate (optional; the summary's diag(gamma(Ax)) with gamma a
+ *     bottleneck MLP on the rank-r projection): gamma(u) =
+ *     sigmoid(W2 relu(W1 u + c1) + c2), W1 [h][r], c1 [h], W2 [r][h], c2 [r]
+ *     (fp32 parameters), applied rank by rank, on top of the scalar gate:
+ *     e = act_m g_m alpha sum_j B[n][j] gamma_j(u) u_j.  h = 0 (no vector
+ *     gate) is the scalar form above; b = +inf (g = 1) with a soft gate is the
+ *     summary's form W + alpha B diag(gamma(Ax)) A.
  *   - Codes: signed codes q in [-8,7] are stored offset-binary u = q + 8 with
  *     zero point 8; unsigned codes u in [0,15] carry a per-channel zero point.
  *     Dequantised weight w = s_n * (u - z_n).
@@ -206,7 +213,7 @@ void oracle_gate(const uint16_t *x, int64_t M, int64_t K, const uint16_t *w_g, f
  * down-projection u (length r) is passed in, computed once per token. */
 static double linear_element(const uint16_t *xrow, int64_t K, int64_t n,
                              const uint8_t *packed, const float *scales, const uint8_t *zeros,
-                             const double *u, const uint16_t *B, int64_t r, float g, int active)
+                             const double *u, const uint16_t *B, int64_t r, double g, int active)
 {
     double y0 = 0.0;
     for (int64_t k = 0; k < K; k++)
@@ -216,7 +223,7 @@ static double linear_element(const uint16_t *xrow, int64_t K, int64_t n,
     double e = 0.0;
     for (int64_t j = 0; j < r; j++)
         e += (double)bf16_to_float(B[n * r + j]) * u[j];
-    return y0 + (double)g * e;
+    return y0 + g * e;
 }
 
 /* EC down-projection of one token: u[j] = sum_k A[j][k] x[k]. */
@@ -231,6 +238,58 @@ static void ec_down(const uint16_t *xrow, int64_t K, const uint16_t *A, int64_t 
 }
 
 #define ORACLE_MAX_RANK 1024
+#define ORACLE_MAX_HIDDEN 1024
+
+/* Vector gate of one token [P4-2.1A]: gamma_j = sigmoid(c2[j] + sum_i
+ * W2[j][i] relu(c1[i] + sum_l W1[i][l] u[l])), in fp64 from fp32 parameters.
+ * The EC then uses gamma_j u_j in place of u_j. */
+static void vector_gate(const double *u, int64_t r, int64_t h, const float *W1,
+                        const float *c1, const float *W2, const float *c2, double *ug)
+{
+    double hid[ORACLE_MAX_HIDDEN];
+    for (int64_t i = 0; i < h; i++) {
+        double s = (double)c1[i];
+        for (int64_t l = 0; l < r; l++)
+            s += (double)W1[i * r + l] * u[l];
+        hid[i] = s > 0.0 ? s : 0.0;
+    }
+    for (int64_t j = 0; j < r; j++) {
+        double s = (double)c2[j];
+        for (int64_t i = 0; i < h; i++)
+            s += (double)W2[j * h + i] * hid[i];
+        ug[j] = (1.0 / (1.0 + exp(-s))) * u[j];
+    }
+}
+
+/* Optional vector-gate parameters (h = 0: none). */
+typedef struct {
+    int64_t h;
+    const float *W1, *c1, *W2, *c2;
+    double alpha;
+} oracle_vgate;
+
+/* Per-token EC set-up shared by the full and the sampled layer: gate value,
+ * selection, and the rank vector the up-projection contracts with (u, or
+ * gamma(u) u with the vector gate).  Returns the token's EC scale g alpha. */
+static double token_ec(const uint16_t *xrow, int64_t K, const uint16_t *A, int64_t r,
+                       const uint16_t *w_g, float b, double t, int hard,
+                       const oracle_vgate *vg, int *active, double *u)
+{
+    double z = gate_logit(xrow, w_g, K, b);
+    float g = sigmoid_f(z);
+    *active = token_active(z, t, hard);
+    if (!*active)
+        return 0.0;
+    ec_down(xrow, K, A, r, u);
+    if (vg->h > 0) {
+        double ug[ORACLE_MAX_RANK];
+        vector_gate(u, r, vg->h, vg->W1, vg->c1, vg->W2, vg->c2, ug);
+        for (int64_t j = 0; j < r; j++)
+            u[j] = ug[j];
+        return (double)g * vg->alpha;
+    }
+    return (double)g;
+}
 
 /*
  * Full layer: y[m][n] for all m < M, n < N (fp64 out).  has_ec = 0 gives the
@@ -240,24 +299,24 @@ static void ec_down(const uint16_t *xrow, int64_t K, const uint16_t *A, int64_t 
 int oracle_w4_linear(const uint16_t *x, int64_t M, int64_t K, int64_t N,
                      const uint8_t *packed, const float *scales, const uint8_t *zeros,
                      int has_ec, const uint16_t *A, const uint16_t *B, int64_t r,
-                     const uint16_t *w_g, float b, float tau, int hard, double *y)
+                     const uint16_t *w_g, float b, float tau, int hard,
+                     int64_t gate_h, const float *W1, const float *c1, const float *W2,
+                     const float *c2, float alpha, double *y)
 {
     if (has_ec && (r < 1 || r > ORACLE_MAX_RANK))
         return -1;
+    if (gate_h < 0 || gate_h > ORACLE_MAX_HIDDEN)
+        return -3;
+    const oracle_vgate vg = {gate_h, W1, c1, W2, c2, (double)alpha};
     double t = oracle_logit_threshold(tau);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t m = 0; m < M; m++) {
         const uint16_t *xrow = x + m * K;
         double u[ORACLE_MAX_RANK];
-        float g = 0.0f;
+        double g = 0.0;
         int active = 0;
-        if (has_ec) {
-            double z = gate_logit(xrow, w_g, K, b);
-            g = sigmoid_f(z);
-            active = token_active(z, t, hard);
-            if (active)
-                ec_down(xrow, K, A, r, u);
-        }
+        if (has_ec)
+            g = token_ec(xrow, K, A, r, w_g, b, t, hard, &vg, &active, u);
         for (int64_t n = 0; n < N; n++)
             y[m * N + n] = linear_element(xrow, K, n, packed, scales, zeros,
                                           has_ec ? u : NULL, B, r, g, active);
@@ -273,27 +332,27 @@ int oracle_w4_linear_sampled(const uint16_t *x, int64_t M, int64_t K, int64_t N,
                              const uint8_t *packed, const float *scales, const uint8_t *zeros,
                              int has_ec, const uint16_t *A, const uint16_t *B, int64_t r,
                              const uint16_t *w_g, float b, float tau, int hard,
+                             int64_t gate_h, const float *W1, const float *c1, const float *W2,
+                             const float *c2, float alpha,
                              int64_t S, const int64_t *ms, const int64_t *ns, double *y_s)
 {
     if (has_ec && (r < 1 || r > ORACLE_MAX_RANK))
         return -1;
+    if (gate_h < 0 || gate_h > ORACLE_MAX_HIDDEN)
+        return -3;
     for (int64_t i = 0; i < S; i++)
         if (ms[i] < 0 || ms[i] >= M || ns[i] < 0 || ns[i] >= N)
             return -2;
+    const oracle_vgate vg = {gate_h, W1, c1, W2, c2, (double)alpha};
     double t = oracle_logit_threshold(tau);
 #pragma omp parallel for schedule(dynamic, 16)
     for (int64_t i = 0; i < S; i++) {
         const uint16_t *xrow = x + ms[i] * K;
         double u[ORACLE_MAX_RANK];
-        float g = 0.0f;
+        double g = 0.0;
         int active = 0;
-        if (has_ec) {
-            double z = gate_logit(xrow, w_g, K, b);
-            g = sigmoid_f(z);
-            active = token_active(z, t, hard);
-            if (active)
-                ec_down(xrow, K, A, r, u);
-        }
+        if (has_ec)
+            g = token_ec(xrow, K, A, r, w_g, b, t, hard, &vg, &active, u);
         y_s[i] = linear_element(xrow, K, ns[i], packed, scales, zeros,
                                 has_ec ? u : NULL, B, r, g, active);
     }

@@ -348,3 +348,151 @@ def test_generator_workloads_shapes_and_rates():
     for cfg in (1, 2, 4):
         d = gen.make(cfg)
         assert d["codes"].shape == (d["N"], d["K"])
+
+
+# ------------------------------------------------- vector gate (summary 2.1 A)
+# gamma(u) = sigmoid(W2 relu(W1 u + c1) + c2) on the rank-r projection u = A x,
+# applied rank by rank on top of the scalar gate.  Each pin reduces a choice of
+# MLP parameters to a form already pinned above (the scalar-gate layer with A
+# and B restricted to some ranks) or to exact arithmetic on it.
+
+def vgate(ec, h, W1=None, c1=None, W2=None, c2=None, alpha=1.0):
+    r = ec["A"].shape[0]
+    z = lambda *s: np.zeros(s, np.float32)
+    return dict(ec, gate_h=h, alpha=alpha,
+                gate_w1=z(h, r) if W1 is None else np.asarray(W1, np.float32),
+                gate_c1=z(h) if c1 is None else np.asarray(c1, np.float32),
+                gate_w2=z(r, h) if W2 is None else np.asarray(W2, np.float32),
+                gate_c2=z(r) if c2 is None else np.asarray(c2, np.float32))
+
+
+def restrict_ranks(ec, keep):
+    """The scalar-gate EC with only the ranks in `keep` (A rows, B columns)."""
+    A = ec["A"].copy()
+    B = ec["B"].copy()
+    drop = np.setdiff1d(np.arange(A.shape[0]), keep)
+    A[drop] = 0
+    B[:, drop] = 0
+    return dict(ec, A=A, B=B)
+
+
+@pytest.mark.parametrize("hard", [0, 1])
+def test_vector_gate_constant_one_is_scalar_form(hard):
+    """W1 = W2 = 0, c2 = +inf: gamma = 1 for every rank, so the layer equals the
+    scalar-gate layer bit for bit (whatever W1, c1 hold)."""
+    rng = np.random.default_rng(30 + hard)
+    M, K, N, r, h = 6, 96, 20, 8, 3
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_U4, hard, tau=0.5)
+    want = oracle.w4_linear(x, p, s, z, ec)
+    e = vgate(ec, h, W1=rng.normal(size=(h, r)), c1=rng.normal(size=h),
+              c2=np.full(r, np.inf))
+    assert np.array_equal(oracle.w4_linear(x, p, s, z, e), want)
+
+
+def test_vector_gate_half_and_alpha():
+    """W1 = W2 = 0, c2 = 0: gamma = 1/2 exactly, so the EC term is half the
+    scalar form's; alpha = 2 restores it; the EC term is linear in alpha."""
+    rng = np.random.default_rng(32)
+    M, K, N, r, h = 5, 64, 16, 8, 2
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_S4)
+    y0 = oracle.w4_linear(x, p, s, z, None)
+    y1 = oracle.w4_linear(x, p, s, z, ec)
+    yh = oracle.w4_linear(x, p, s, z, vgate(ec, h))
+    np.testing.assert_allclose(2 * (yh - y0), y1 - y0, rtol=1e-12, atol=1e-15)
+    ya = oracle.w4_linear(x, p, s, z, vgate(ec, h, alpha=2.0))
+    np.testing.assert_allclose(ya, y1, rtol=1e-13, atol=1e-15)
+    y3 = oracle.w4_linear(x, p, s, z, vgate(ec, h, alpha=3.0))
+    np.testing.assert_allclose(y3 - y0, 3 * (yh - y0), rtol=1e-12, atol=1e-15)
+
+
+def test_vector_gate_rank_selector():
+    """W2 = 0, c2_j = +inf for the ranks in S and -inf elsewhere: gamma is the
+    indicator of S, so the layer equals the scalar-gate layer with A and B
+    restricted to S, bit for bit."""
+    rng = np.random.default_rng(33)
+    M, K, N, r, h = 6, 64, 24, 8, 4
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_U4, 1, tau=0.45)
+    S = np.array([1, 4, 5, 7])
+    c2 = np.full(r, -np.inf, np.float32)
+    c2[S] = np.inf
+    got = oracle.w4_linear(x, p, s, z, vgate(ec, h, c2=c2))
+    assert np.array_equal(got, oracle.w4_linear(x, p, s, z, restrict_ranks(ec, S)))
+
+
+def test_vector_gate_hidden_routing_and_relu():
+    """One hidden unit i0 reads rank j0 (W1 = e_i0 e_j0^T, c1 = 0) and drives
+    every rank through W2[:, i0] = +-1e30 (+ on S): for a token with u_j0 > 0
+    gamma is the indicator of S; with u_j0 <= 0 the ReLU gives 0 and gamma = 1/2.
+    A transposed W1 or W2, a wrong hidden index or a missing ReLU fails."""
+    rng = np.random.default_rng(34)
+    M, K, N, r, h = 12, 64, 16, 8, 3
+    i0, j0 = 2, 5
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_S4)
+    W1 = np.zeros((h, r), np.float32)
+    W1[i0, j0] = 1.0
+    S = np.array([0, 3, 6])
+    W2 = np.zeros((r, h), np.float32)
+    W2[:, i0] = -1e30
+    W2[S, i0] = 1e30
+    got = oracle.w4_linear(x, p, s, z, vgate(ec, h, W1=W1, W2=W2))
+    sel = oracle.w4_linear(x, p, s, z, restrict_ranks(ec, S))
+    half = oracle.w4_linear(x, p, s, z, vgate(ec, h))          # gamma = 1/2
+    uj0 = f32(x).astype(np.float64) @ f32(ec["A"]).astype(np.float64)[j0]
+    pos = uj0 > 0
+    assert pos.any() and (~pos).any()
+    assert np.array_equal(got[pos], sel[pos])
+    assert np.array_equal(got[~pos], half[~pos])
+
+
+def test_vector_gate_hidden_bias_shuts_units():
+    """c1 = -1e30 drives every hidden unit to 0 through the ReLU, so gamma =
+    sigmoid(c2) whatever W1 and W2 hold: with c2 = 0 it is the gamma = 1/2 layer."""
+    rng = np.random.default_rng(35)
+    M, K, N, r, h = 4, 64, 12, 8, 4
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_U4)
+    e = vgate(ec, h, W1=rng.normal(size=(h, r)), c1=np.full(h, -1e30),
+              W2=rng.normal(size=(r, h)))
+    assert np.array_equal(oracle.w4_linear(x, p, s, z, e), oracle.w4_linear(x, p, s, z, vgate(ec, h)))
+
+
+def test_vector_gate_effective_weight_identity():
+    """Per token, the layer with a vector gate equals x applied to the dense
+    effective weight W + g alpha B diag(gamma) A (summary 2.1 A), with gamma
+    known from the routing construction above (indicator of S, or 1/2)."""
+    rng = np.random.default_rng(36)
+    M, K, N, r, h = 8, 96, 24, 8, 2
+    i0, j0 = 1, 2
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_U4, 1, tau=0.4)
+    W1 = np.zeros((h, r), np.float32)
+    W1[i0, j0] = 1.0
+    S = np.array([2, 3])
+    W2 = np.zeros((r, h), np.float32)
+    W2[:, i0] = -1e30
+    W2[S, i0] = 1e30
+    alpha = 1.5
+    y = oracle.w4_linear(x, p, s, z, vgate(ec, h, W1=W1, W2=W2, alpha=alpha))
+    W = oracle.dequant_w4(p, s, z, K).astype(np.float64)
+    A = f32(ec["A"]).astype(np.float64)
+    B = f32(ec["B"]).astype(np.float64)
+    X = f32(x).astype(np.float64)
+    gt = oracle.gate(x, ec["w_g"], ec["b"], ec["tau"], ec["hard"])
+    for m in range(M):
+        gm = float(gt["g"][m]) if m in gt["idx"] else 0.0
+        gam = np.full(r, 0.5)
+        if X[m] @ A[j0] > 0:
+            gam = np.zeros(r)
+            gam[S] = 1.0
+        Weff = W + gm * alpha * (B @ np.diag(gam) @ A)
+        np.testing.assert_allclose(y[m], Weff @ X[m], rtol=1e-12, atol=1e-12)
+
+
+def test_vector_gate_sampled_matches_full():
+    rng = np.random.default_rng(37)
+    M, K, N, r, h = 7, 64, 20, 16, 4
+    codes, p, s, z, x, ec = rand_layer(rng, M, K, N, r, oracle.CODES_S4, 1, 0.45)
+    e = vgate(ec, h, W1=rng.normal(0, 0.5, (h, r)), c1=rng.normal(0, 0.1, h),
+              W2=rng.normal(0, 0.5, (r, h)), c2=rng.normal(0, 0.5, r), alpha=0.75)
+    y = oracle.w4_linear(x, p, s, z, e)
+    assert not np.array_equal(y, oracle.w4_linear(x, p, s, z, ec))
+    ms, ns = rng.integers(0, M, 50), rng.integers(0, N, 50)
+    assert np.array_equal(oracle.w4_linear_sampled(x, p, s, z, e, ms, ns), y[ms, ns])
