@@ -28,8 +28,16 @@
  *   z_m   = b + sum_k x[m][k] w_g[k]                  (gate logit, fp64 sum)
  *   g_m   = 1 / (1 + exp(-z_m))                       (fp32)
  *   act_m = hard ? (z_m > log(tau / (1 - tau))) : 1   (a tie skips)
+ *   u_m[j] = sum_k A[j][k] x[m][k]                     (EC down-projection)
  *   y[m][n] = s_n sum_k x[m][k] (u[n][k] - z_n)
- *           + act_m g_m sum_j B[n][j] sum_k A[j][k] x[m][k]
+ *           + act_m g_m sum_j B[n][j] u_m[j]
+ *
+ * Optional vector gate (the summary's diag(gamma(Ax)), gamma a bottleneck MLP
+ * on the rank-r projection): with gate_h > 0 the EC term becomes
+ *           act_m g_m alpha sum_j B[n][j] gamma_j(u_m) u_m[j],
+ *   gamma(u) = sigmoid(W2 relu(W1 u + c1) + c2),  W1 [h][r], c1 [h],
+ *   W2 [r][h], c2 [r] (fp32).  With b = +inf (g = 1) and a soft gate this is
+ *   the summary's W + alpha B diag(gamma(Ax)) A.
  *
  * Conventions shared by every entry point:
  *   - Data pointers are DEVICE pointers unless stated otherwise.  The caller
@@ -61,7 +69,7 @@
 extern "C" {
 #endif
 
-#define SPEAR_ABI_VERSION 1
+#define SPEAR_ABI_VERSION 2
 
 typedef uint16_t spear_bf16; /* raw bfloat16 bits */
 typedef int32_t spear_status;
@@ -101,6 +109,8 @@ typedef int32_t spear_status;
 
 /* Largest EC rank accepted; the rank must also be a multiple of 8. */
 #define SPEAR_MAX_RANK 256
+/* Largest hidden width of the optional vector gate's MLP. */
+#define SPEAR_MAX_GATE_HIDDEN 64
 
 /* Quantised weights (all device pointers). */
 typedef struct spear_w4 {
@@ -123,6 +133,14 @@ typedef struct spear_ec {
     float *g_out;             /* optional [M]: g_m                                  */
     int32_t *idx_out;         /* optional [M]: ascending indices of active tokens   */
     int32_t *n_active_out;    /* optional [1]: number of active tokens              */
+    /* Optional vector gate (gate_h == 0: none; the other fields are then unused).
+       Source: summary section 2.1 A.  All fp32, 4-byte aligned device pointers. */
+    int32_t gate_h;           /* hidden width h, 0 or 1 .. SPEAR_MAX_GATE_HIDDEN     */
+    float alpha;              /* scale of the vector-gated EC term                  */
+    const float *gate_w1;     /* [h][r]                                             */
+    const float *gate_c1;     /* [h]                                                */
+    const float *gate_w2;     /* [r][h]                                             */
+    const float *gate_c2;     /* [r]                                                */
 } spear_ec;
 
 /*
@@ -191,6 +209,8 @@ spear_status spear_workspace_init(void *ws, size_t bytes, void *stream);
  * selection and EC down-projection run in the same kernel as the weight
  * stream, and the EC is applied in its epilogue); M > 16 takes the prefill
  * path (an EC pre-pass, then the MFMA GEMM with the EC in its epilogue).
+ * The vector gate is formed where v is formed: in the fused decode kernel's
+ * epilogue, or at the end of the EC pre-pass.
  * The result does not depend on the path beyond fp32 rounding order.
  */
 spear_status spear_w4_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,

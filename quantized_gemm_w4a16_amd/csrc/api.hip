@@ -348,6 +348,13 @@ static spear_status validate_linear(const spear_bf16 *x, int64_t M, const spear_
         return SPEAR_E_ARG;
     if (ec && (isnan(ec->tau) || isnan(ec->b) || (ec->hard != 0 && ec->hard != 1)))
         return SPEAR_E_ARG;
+    if (ec && (ec->gate_h < 0 || ec->gate_h > SPEAR_MAX_GATE_HIDDEN))
+        return SPEAR_E_SHAPE;
+    if (ec && ec->gate_h > 0 &&
+        (!ec->gate_w1 || !ec->gate_c1 || !ec->gate_w2 || !ec->gate_c2))
+        return SPEAR_E_NULL;
+    if (ec && ec->gate_h > 0 && isnan(ec->alpha))
+        return SPEAR_E_ARG;
     if (path == SPEAR_PATH_AUTO)
         path = M <= 16 ? SPEAR_PATH_DECODE : SPEAR_PATH_PREFILL;
     if ((path == SPEAR_PATH_DECODE || path == SPEAR_PATH_DECODE_2PASS) && M > 16)
@@ -358,6 +365,10 @@ static spear_status validate_linear(const spear_bf16 *x, int64_t M, const spear_
     if (ec && (!aligned(ec->A, 16) || !aligned(ec->B, 16) || !aligned(ec->w_gate, 16) ||
                !aligned(ec->g_out, 4) || !aligned(ec->idx_out, 4) ||
                !aligned(ec->n_active_out, 4)))
+        return SPEAR_E_ALIGN;
+    if (ec && ec->gate_h > 0 &&
+        (!aligned(ec->gate_w1, 4) || !aligned(ec->gate_c1, 4) || !aligned(ec->gate_w2, 4) ||
+         !aligned(ec->gate_c2, 4)))
         return SPEAR_E_ALIGN;
     const int32_t r = ec ? ec->r : 0;
     const WsLayout L = ws_layout(M, N, K, r);
@@ -435,14 +446,26 @@ static spear_status run_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w
         a.g_out = ec->g_out;
         a.idx_out = ec->idx_out;
         a.nact_out = ec->n_active_out;
+        if (ec->gate_h > 0) {
+            a.gate_h = ec->gate_h;
+            a.alpha = ec->alpha;
+            a.gw1 = ec->gate_w1;
+            a.gc1 = ec->gate_c1;
+            a.gw2 = ec->gate_w2;
+            a.gc2 = ec->gate_c2;
+        }
     }
 
     hipError_t e = hipSuccess;
     const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + L.active);
     switch (path) {
     case SPEAR_PATH_DECODE:
-        e = launch_decode(a, ec ? 1 : 0, s);
-        break;
+        if (!(ec && ec->gate_h > 0)) {
+            e = launch_decode(a, ec ? 1 : 0, s);
+            break;
+        }
+        // the vector gate is formed by the pre-pass: two launches
+        [[fallthrough]];
     case SPEAR_PATH_DECODE_2PASS:
         if (ec) {
             e = launch_prepass(a, s);

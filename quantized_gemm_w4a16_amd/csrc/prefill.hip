@@ -56,7 +56,38 @@ struct PreShared {
     float *g;                 // [16]
     int *act;                 // [16]
     uint32_t *tag, *bad;
+    float *hid;               // [16][SPEAR_MAX_GATE_HIDDEN]: vector gate's hidden layer
 };
+
+// Vector gate of tokens m0 .. m0 + 15 (summary section 2.1 A: a bottleneck MLP
+// on the rank-r projection): hid[m][i] = relu(c1[i] + sum_l W1[i][l] u_m[l])
+// for every token slot, by all threads of the workgroup (nthreads); u_m[l] is
+// read from the pre-pass layout (tile l / 16, lane 16 ((l % 16) / 4) + m,
+// element l % 4).  The caller synchronises before reading hid.
+__device__ void vgate_hidden(const LinearArgs &a, const f32x4 (*s_uw)[64], float *hid, int tid,
+                             int nthreads)
+{
+    const int h = a.gate_h, r = a.r;
+    for (int q = tid; q < 16 * h; q += nthreads) {
+        const int m = q & 15, i = q >> 4;
+        float s = a.gc1[i];
+        const float *w1 = a.gw1 + (int64_t)i * r;
+        for (int l = 0; l < r; l++)
+            s = __builtin_fmaf(w1[l], s_uw[l >> 4][16 * ((l & 15) >> 2) + m][l & 3], s);
+        hid[m * SPEAR_MAX_GATE_HIDDEN + i] = s > 0.f ? s : 0.f;
+    }
+}
+
+// gamma_j of token slot m from its hidden layer: sigmoid(c2[j] + sum_i W2[j][i] hid[m][i]).
+__device__ __forceinline__ float vgate_gamma(const LinearArgs &a, const float *hid, int m, int j)
+{
+    const int h = a.gate_h;
+    float s = a.gc2[j];
+    const float *w2 = a.gw2 + (int64_t)j * h;
+    for (int i = 0; i < h; i++)
+        s = __builtin_fmaf(w2[i], hid[m * SPEAR_MAX_GATE_HIDDEN + i], s);
+    return 1.f / (1.f + __expf(-s));
+}
 
 // The last step of the pre-pass for tokens m0 .. m0 + 15, given their logit
 // sums (without b) in s_zw and u in s_uw (tile t, lane l: ranks 16 t + 4 (l / 16)
@@ -65,8 +96,8 @@ struct PreShared {
 // when tagged).  bad (an expired wait upstream): the group's sums are
 // incomplete, so g and v are NaN and each real token's selection flag is -1.
 __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_uw)[64],
-                               const double *s_zw, float *s_g, int *s_act, int tid, int lane,
-                               int wave, int nwaves, bool tagged, uint32_t tag, bool bad)
+                               const double *s_zw, float *s_g, int *s_act, float *s_hid, int tid,
+                               int lane, int wave, int nwaves, bool tagged, uint32_t tag, bool bad)
 {
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, m = m0 + lr;
@@ -86,15 +117,20 @@ __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_
         if (mm < M && a.g_out)
             a.g_out[mm] = g;
     }
+    const bool vg = a.gate_h > 0;
+    if (vg)
+        vgate_hidden(a, s_uw, s_hid, tid, 64 * nwaves);
     __syncthreads();
     // rows m >= M (up to the 16-row padding) get v = 0
-    const float g = s_act[lr] ? s_g[lr] : 0.f;
+    const float g = s_act[lr] ? (vg ? s_g[lr] * a.alpha : s_g[lr]) : 0.f;
     for (int tile = wave; wave < nwaves && tile < rpad / 16; tile += nwaves) {
         const f32x4 u = s_uw[tile][lane];
         uint16_t hi[4], lo[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-            const float v = g * u[i];
+            const int j = 16 * tile + 4 * lg + i;
+            const float gam = (vg && j < a.r) ? vgate_gamma(a, s_hid, lr, j) : 1.f;
+            const float v = g * (gam * u[i]);
             hi[i] = f2bf(v);
             lo[i] = f2bf(v - bf16f(hi[i]));
         }
@@ -336,7 +372,8 @@ __device__ __forceinline__ void prepass_tail(const LinearArgs &a, const int64_t 
         if (bad && tid == 0)          // an expired wait: counted; the group's v is NaN
             atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
     }
-    prepass_finish(a, m0, sh.uw, sh.zw, sh.g, sh.act, tid, lane, wave, PW, tagged, tag, bad);
+    prepass_finish(a, m0, sh.uw, sh.zw, sh.g, sh.act, sh.hid, tid, lane, wave, PW, tagged, tag,
+                   bad);
 }
 
 __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArgs a)
@@ -349,11 +386,13 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
     __shared__ float s_g[16];
     __shared__ int s_act[16];
     __shared__ uint32_t s_tag, s_bad;
+    __shared__ float s_hid[16 * SPEAR_MAX_GATE_HIDDEN];
     pin_args(a);
     uint64_t claimed = opaque_zero64();
     if (a.pre_ks > 1 && threadIdx.x == 0)
         claimed = epoch_claim(a);                         // back long before it is used
-    const PreShared<PRE_WAVES> sh = {s_u, s_u + PRE_WAVES / 2, s_z, s_wg, s_uw, s_zw, s_g, s_act, &s_tag, &s_bad};
+    const PreShared<PRE_WAVES> sh = {s_u, s_u + PRE_WAVES / 2, s_z, s_wg, s_uw, s_zw, s_g, s_act,
+                                     &s_tag, &s_bad, s_hid};
     prepass_body<PRE_WAVES>(a, blockIdx.x, sh, claimed, false);
 }
 
@@ -392,6 +431,7 @@ __global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
     __shared__ float s_g[16];
     __shared__ int s_act[16];
     __shared__ uint32_t s_tag, s_bad;
+    __shared__ float s_hid[16 * SPEAR_MAX_GATE_HIDDEN];
     uint8_t *const ring[RING] = {s_r0, s_r1, s_r2};
     pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63;
@@ -501,7 +541,7 @@ __global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
     // the workgroup's partials: waves in order (then lane groups for z)
     f32x4 (*su)[NT][64] = reinterpret_cast<f32x4(*)[NT][64]>(s_r0);
     const PreShared<8> sh = {nullptr, nullptr, s_z, nullptr, reinterpret_cast<f32x4(*)[64]>(s_r1), s_zw, s_g,
-                             s_act, &s_tag, &s_bad};
+                             s_act, &s_tag, &s_bad, s_hid};
 #pragma unroll
     for (int t = 0; t < NT; t++)
         su[wave][t][lane] = acc[t];
@@ -636,7 +676,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
             constexpr int PW = G2_NT / 64;
             constexpr int CB = G2_ST > 4 ? G2_XB : G2_WBS;
             static_assert((PW / 2) * PRE_RT * 64 * 16 <= G2_XB && PRE_TILES * 64 * 16 <= G2_XB &&
-                          PW * 64 * 8 + PW * 4 * PRE_T * 16 <= CB && 16 * 16 + 8 <= CB,
+                          PW * 64 * 8 + PW * 4 * PRE_T * 16 <= CB &&
+                          512 + 16 * SPEAR_MAX_GATE_HIDDEN * 4 <= CB,
                           "pre-pass LDS inside the stage buffers");
             uint8_t *const c0 = G2_ST > 4 ? s_x3 : s_w0;
             uint8_t *const c1 = G2_ST > 4 ? s_x4 : s_w1;
@@ -650,7 +691,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                 reinterpret_cast<float *>(c1 + 128),
                 reinterpret_cast<int *>(c1 + 192),
                 reinterpret_cast<uint32_t *>(c1 + 256),
-                reinterpret_cast<uint32_t *>(c1 + 260)};
+                reinterpret_cast<uint32_t *>(c1 + 260),
+                reinterpret_cast<float *>(c1 + 512)};
             if ((int64_t)blockIdx.x < ((a.M + 15) / 16) * a.pre_ks)
                 prepass_body<PW>(a, blockIdx.x, sh, claimed, true);
             return;

@@ -164,6 +164,9 @@ struct LinearArgs {
     int64_t g_bn;    // MFMA GEMM: channels per tile (64 with 64-token tiles, else 256)
     int64_t g_ks;    // MFMA GEMM: K slices per tile (partials reduced by a second launch)
     int64_t npre;    // K-split GEMM with the EC pre-pass in its launch: leading pre-pass blocks
+    const float *gw1, *gc1, *gw2, *gc2;   // vector gate MLP (gate_h > 0)
+    int32_t gate_h;
+    float alpha;
     WsLayout L;
     uint32_t wait_limit;
     int32_t out_f32;
@@ -205,6 +208,7 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.splitp); pin_arg(a.L.pu);
     pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);
+    pin_arg(a.gw1); pin_arg(a.gc1); pin_arg(a.gw2); pin_arg(a.gc2); pin_arg(a.gate_h); pin_arg(a.alpha);
 }
 
 // ---------------------------------------------- tagged cross-workgroup exchange

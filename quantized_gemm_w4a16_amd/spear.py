@@ -28,6 +28,8 @@ PATH_PREFILL = 2
 PATH_DECODE_2PASS = 3
 PATH_PREFILL_LARGE = 4
 MAX_RANK = 256
+MAX_GATE_HIDDEN = 64
+ABI_VERSION = 2
 
 EXPORTS = ("spear_pack_w4", "spear_gate", "spear_w4_linear_workspace_size",
            "spear_workspace_init", "spear_w4_linear", "spear_w4_linear_path",
@@ -51,7 +53,10 @@ class _EC(ctypes.Structure):
     _fields_ = [("A", ctypes.c_void_p), ("B", ctypes.c_void_p), ("w_gate", ctypes.c_void_p),
                 ("b", ctypes.c_float), ("tau", ctypes.c_float), ("hard", ctypes.c_int32),
                 ("r", ctypes.c_int32), ("g_out", ctypes.c_void_p), ("idx_out", ctypes.c_void_p),
-                ("n_active_out", ctypes.c_void_p)]
+                ("n_active_out", ctypes.c_void_p), ("gate_h", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("gate_w1", ctypes.c_void_p),
+                ("gate_c1", ctypes.c_void_p), ("gate_w2", ctypes.c_void_p),
+                ("gate_c2", ctypes.c_void_p)]
 
 
 _lib = None
@@ -125,7 +130,9 @@ class W4:
 class EC:
     """Error compensator on the device: A [r][K], B [N][r], w_gate [K] as bf16
     (torch.bfloat16 or int16 bit tensors), gate bias b, threshold tau, hard flag.
-    Optional outputs g_out [M] fp32, idx_out [M] int32, n_active_out [1] int32."""
+    Optional outputs g_out [M] fp32, idx_out [M] int32, n_active_out [1] int32.
+    Optional vector gate (fp32): gate_w1 [h][r], gate_c1 [h], gate_w2 [r][h],
+    gate_c2 [r] and its scale alpha."""
     A: torch.Tensor
     B: torch.Tensor
     w_gate: torch.Tensor
@@ -135,15 +142,25 @@ class EC:
     g_out: Optional[torch.Tensor] = None
     idx_out: Optional[torch.Tensor] = None
     n_active_out: Optional[torch.Tensor] = None
+    gate_w1: Optional[torch.Tensor] = None
+    gate_c1: Optional[torch.Tensor] = None
+    gate_w2: Optional[torch.Tensor] = None
+    gate_c2: Optional[torch.Tensor] = None
+    alpha: float = 1.0
 
     @property
     def r(self) -> int:
         return int(self.A.shape[0])
 
+    @property
+    def gate_h(self) -> int:
+        return 0 if self.gate_w1 is None else int(self.gate_w1.shape[0])
+
     def _c(self):
         return _EC(_ptr(self.A), _ptr(self.B), _ptr(self.w_gate), float(self.b), float(self.tau),
                    int(self.hard), self.r, _ptr(self.g_out), _ptr(self.idx_out),
-                   _ptr(self.n_active_out))
+                   _ptr(self.n_active_out), self.gate_h, float(self.alpha), _ptr(self.gate_w1),
+                   _ptr(self.gate_c1), _ptr(self.gate_w2), _ptr(self.gate_c2))
 
 
 def spear_abi_version() -> int:

@@ -34,6 +34,12 @@ def gpu_ec(ec, M, outputs=True):
     if ec is None:
         return None
     e = sp.EC(dev(ec["A"]), dev(ec["B"]), dev(ec["w_g"]), ec["b"], ec["tau"], ec["hard"])
+    if ec.get("gate_h", 0):
+        e.gate_w1 = dev(np.asarray(ec["gate_w1"], np.float32))
+        e.gate_c1 = dev(np.asarray(ec["gate_c1"], np.float32))
+        e.gate_w2 = dev(np.asarray(ec["gate_w2"], np.float32))
+        e.gate_c2 = dev(np.asarray(ec["gate_c2"], np.float32))
+        e.alpha = float(ec.get("alpha", 1.0))
     if outputs:
         e.g_out = torch.full((max(M, 1),), -1.0, dtype=torch.float32, device="cuda")
         e.idx_out = torch.full((max(M, 1),), -1, dtype=torch.int32, device="cuda")

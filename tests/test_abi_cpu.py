@@ -32,7 +32,7 @@ def test_exports_every_declared_symbol(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(sp.EXPORTS)
-    assert lib.spear_abi_version() == 1
+    assert lib.spear_abi_version() == sp.ABI_VERSION == 2
 
 
 def test_status_strings(lib):
@@ -75,8 +75,9 @@ def linear(lib, x=A16, M=4, N=64, K=128, ec=None, y=A16, out=1, ws=A16, wsb=1 <<
                                     y, out, ws, wsb, path, None)
 
 
-def ec_struct(r=16, tau=0.5, hard=0, A=A16, B=A16, wg=A16, b=0.0):
-    return sp._EC(A, B, wg, b, tau, hard, r, None, None, None)
+def ec_struct(r=16, tau=0.5, hard=0, A=A16, B=A16, wg=A16, b=0.0, gate_h=0, alpha=1.0,
+              w1=A16, c1=A16, w2=A16, c2=A16):
+    return sp._EC(A, B, wg, b, tau, hard, r, None, None, None, gate_h, alpha, w1, c1, w2, c2)
 
 
 def test_linear_validation(lib):
@@ -103,6 +104,16 @@ def test_linear_validation(lib):
     assert linear(lib, ec=ec_struct(B=A16 + 2)) == E_ALIGN
     need = sp.spear_w4_linear_workspace_size(4, 64, 128, 16)
     assert linear(lib, ec=ec_struct(), wsb=need - 1) == E_WS
+    # the vector gate's MLP
+    assert linear(lib, ec=ec_struct(gate_h=65)) == E_SHAPE
+    assert linear(lib, ec=ec_struct(gate_h=-1)) == E_SHAPE
+    assert linear(lib, ec=ec_struct(gate_h=4, w1=None)) == E_NULL
+    assert linear(lib, ec=ec_struct(gate_h=4, c2=None)) == E_NULL
+    assert linear(lib, ec=ec_struct(gate_h=4, alpha=float("nan"))) == E_ARG
+    assert linear(lib, ec=ec_struct(gate_h=4, w2=A16 + 2)) == E_ALIGN
+    # gate_h = 0: the MLP pointers are not read
+    assert linear(lib, ec=ec_struct(gate_h=0, w1=None, c1=None, w2=None, c2=None),
+                  wsb=need - 1) == E_WS
 
 
 def test_pack_and_gate_validation(lib):
