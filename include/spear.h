@@ -210,7 +210,8 @@ spear_status spear_workspace_init(void *ws, size_t bytes, void *stream);
  * stream, and the EC is applied in its epilogue); M > 16 takes the prefill
  * path (an EC pre-pass, then the MFMA GEMM with the EC in its epilogue).
  * The vector gate is formed where v is formed: in the fused decode kernel's
- * epilogue, or at the end of the EC pre-pass.
+ * epilogue (ranks up to 32; larger ranks take the pre-pass form of the decode
+ * path, two launches), or at the end of the EC pre-pass.
  * The result does not depend on the path beyond fp32 rounding order.
  */
 spear_status spear_w4_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,

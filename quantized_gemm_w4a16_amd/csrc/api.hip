@@ -460,11 +460,12 @@ static spear_status run_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w
     const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + L.active);
     switch (path) {
     case SPEAR_PATH_DECODE:
-        if (!(ec && ec->gate_h > 0)) {
+        if (!(ec && ec->gate_h > 0 && a.rpad > 32)) {
             e = launch_decode(a, ec ? 1 : 0, s);
             break;
         }
-        // the vector gate is formed by the pre-pass: two launches
+        // a vector gate over more than one 32-rank block is formed by the
+        // pre-pass: two launches
         [[fallthrough]];
     case SPEAR_PATH_DECODE_2PASS:
         if (ec) {

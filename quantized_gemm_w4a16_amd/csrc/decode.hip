@@ -81,6 +81,47 @@ constexpr size_t EC_LDS_U = DEC_WAVES * 64 * 8 * sizeof(float);   // u partials 
 static_assert(EC_LDS_U >= DEC_WAVES * 16 * 32 * sizeof(float), "consumer u exchange");
 constexpr size_t EC_LDS_Z = DEC_WAVES * 64 * sizeof(double);      // gate-logit partials
 constexpr size_t EC_LDS = EC_LDS_U + EC_LDS_Z + 64;               // + tag and flags
+// the vector gate's u [16][32] and hidden layer [16][SPEAR_MAX_GATE_HIDDEN], after EC_LDS
+constexpr size_t EC_LDS_VG = (16 * 32 + 16 * SPEAR_MAX_GATE_HIDDEN) * sizeof(float);
+
+// Vector gate of the fused decode (ranks up to 32, one rank block; summary
+// section 2.1 A): wave 0, lane (lr, lg) holding ranks 8 lg .. 8 lg + 7 of token
+// lr in (ua, ub), replaces them by gamma_j(u) u_j, gamma(u) = sigmoid(W2 relu(W1
+// u + c1) + c2).  The token's u and hidden layer go through wave-local LDS
+// (only wave 0 touches vl).
+__device__ __forceinline__ void vgate_fused(const LinearArgs &a, float *vl, int lr, int lg,
+                                            f32x4 &ua, f32x4 &ub)
+{
+    const int h = a.gate_h, r = a.r;
+    float *vu = vl, *hid = vl + 16 * 32;
+    *reinterpret_cast<f32x4 *>(vu + lr * 32 + 8 * lg) = ua;
+    *reinterpret_cast<f32x4 *>(vu + lr * 32 + 8 * lg + 4) = ub;
+    wait_lgkmcnt0();
+    for (int i = lg; i < h; i += 4) {
+        float sacc = a.gc1[i];
+        const float *w1 = a.gw1 + (int64_t)i * r;
+        for (int l = 0; l < r; l++)
+            sacc = __builtin_fmaf(w1[l], vu[lr * 32 + l], sacc);
+        hid[lr * SPEAR_MAX_GATE_HIDDEN + i] = sacc > 0.f ? sacc : 0.f;
+    }
+    wait_lgkmcnt0();
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+        const int j = 8 * lg + q;
+        float gam = 1.f;
+        if (j < r) {
+            float sacc = a.gc2[j];
+            const float *w2 = a.gw2 + (int64_t)j * h;
+            for (int i = 0; i < h; i++)
+                sacc = __builtin_fmaf(w2[i], hid[lr * SPEAR_MAX_GATE_HIDDEN + i], sacc);
+            gam = 1.f / (1.f + __expf(-sacc));
+        }
+        if (q < 4)
+            ua[q] *= gam;
+        else
+            ub[q - 4] *= gam;
+    }
+}
 
 // Producer workgroup p: wave w takes K slice [(4p + w) prod_k, +prod_k) and
 // computes, for all 16 token slots, the gate-logit partial (fp64) and
@@ -404,6 +445,8 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                     ua += *reinterpret_cast<const f32x4 *>(lu + w * 16 * 32 + 8 * lg);
                     ub += *reinterpret_cast<const f32x4 *>(lu + w * 16 * 32 + 8 * lg + 4);
                 }
+                if (a.gate_h > 0)
+                    vgate_fused(a, reinterpret_cast<float *>(lds + EC_LDS), lr, lg, ua, ub);
                 const int j = 32 * t + 8 * lg;
                 u32x4 bf;
                 if (t < 2)
@@ -434,6 +477,8 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                     ua += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg);
                     ub += *reinterpret_cast<const f32x4 *>(lu + (w * 16 + lr) * 32 + 8 * lg + 4);
                 }
+                if (a.gate_h > 0)
+                    vgate_fused(a, reinterpret_cast<float *>(lds + EC_LDS), lr, lg, ua, ub);
                 const int j = 32 * t + 8 * lg;
                 u32x4 vh, vl;
 #pragma unroll
@@ -460,7 +505,8 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
         }
     }
     // the gate of the lane's token (token 0 with one token)
-    const float gs = GV ? (__shfl(act, 0) ? __shfl(g, 0) : 0.f) : (act ? g : 0.f);
+    const float ga = a.gate_h > 0 ? a.alpha : 1.f;    // the vector gate's scale
+    const float gs = GV ? (__shfl(act, 0) ? __shfl(g, 0) * ga : 0.f) : (act ? g * ga : 0.f);
     *ok_out = ok;
     if (!ok) {
         // An expired wait: the EC term of every token of this channel group is
@@ -872,8 +918,9 @@ hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
     const dim3 grid((unsigned)(npwg + a.ncg * a.ksplit));
     const dim3 block(64 * DEC_WAVES);
     size_t lds = (size_t)(a.M + 1) * (size_t)(a.spw * 256 + 16);
-    if (EC_MODE == 1 && lds < EC_LDS)
-        lds = EC_LDS;                                     // EC partials meet in the same LDS
+    const size_t ec_lds = EC_LDS + (a.gate_h > 0 ? EC_LDS_VG : 0);
+    if (EC_MODE == 1 && lds < ec_lds)
+        lds = ec_lds;                                     // EC partials meet in the same LDS
     hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW, GV>), grid, block, lds, s, a);
     return hipGetLastError();
 }

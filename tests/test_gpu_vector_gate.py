@@ -55,7 +55,7 @@ def test_vector_gate_one_is_scalar_form_bitwise(M):
     d = random_case(M, 272, 1024, 32, oracle.CODES_S4, 1, seed=800 + M)
     dv = with_vgate(d, 8, seed=5, alpha=1.0, c2=np.full(32, np.inf))
     w = gpu_weights(d)
-    for path in (PATHS[1:] if M <= 16 else PATHS[2:]):
+    for path in (PATHS if M <= 16 else PATHS[2:]):
         y0, _ = run_gpu(d, path=path, w=w)
         y1, _ = run_gpu(dv, path=path, w=w)
         assert np.array_equal(y0, y1), path
