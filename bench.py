@@ -29,6 +29,10 @@ The same line also carries:
 (C1: M = 16, K = N = 1024, launch-latency bound; C3: M = 64, K = 4096,
 N = 14336, rank 64, hard gate; C4: prefill; C5: a 28-layer stack of a
 1.5B-class decoder's seven linears with ECs on 4 layers at --c5-m tokens).
+--workload slo measures the kernel-latency table of the C5 stack's linear
+kinds (2048 -> 2048, 2048 -> 8192, 8192 -> 2048, each with and without its EC)
+at token counts 1 .. 4096, then runs a seeded synthetic request trace through
+continuous batching with the native chunk picker against fixed chunk sizes.
 """
 from __future__ import annotations
 
@@ -60,7 +64,9 @@ def parse():
                    help="leave the C4 prefill object out of the default C2 line")
     p.add_argument("--prefill-steps", type=int, default=20,
                    help="layer calls per replay of the C4 prefill graph in the default line")
-    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    p.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5", "slo"])
+    p.add_argument("--lut-out", default="",
+                   help="slo workload: also write the measured latency table to this JSON file")
     p.add_argument("--c5-m", type=int, default=1, choices=[1, 16, 128, 2048],
                    help="tokens per call of the C5 stack")
     p.add_argument("--copies", type=int, default=64)
@@ -553,6 +559,100 @@ def run_c5(args, torch, sp, gen):
     }
 
 
+def c5_stack(torch, sp, gen, M_max):
+    """The C5 stack's 196 linears on the device (each its own weights), and
+    input / output buffers for up to M_max tokens."""
+    layers = []
+    ec_layers = set(gen.c5_ec_layers())
+    for layer in range(gen.C5_LAYERS):
+        for lin in gen.C5_LINEARS:
+            d = gen.make_c5(layer, lin, 1)
+            codes = dev(d["codes"], torch)
+            w = sp.W4(sp.spear_pack_w4(codes, d["kind"]), dev(d["scales"], torch),
+                      dev(d["zeros"], torch), d["N"], d["K"])
+            del codes
+            e = d["ec"]
+            ec = (sp.EC(dev(e["A"], torch), dev(e["B"], torch), dev(e["w_g"], torch), e["b"],
+                        e["tau"], e["hard"]) if e is not None else None)
+            layers.append((lin, d["N"], d["K"], w, ec, e["r"] if e is not None else 0))
+    xs = {K: dev(gen.make_c5(0, "down" if K == gen.C5_FF else "q", M_max)["x"], torch)
+          for K in (gen.C5_D, gen.C5_FF)}
+    ys = {N: torch.empty((M_max, N), dtype=torch.float32, device="cuda")
+          for N in (gen.C5_D, gen.C5_FF)}
+    need = max(sp.spear_w4_linear_workspace_size(M_max, N, K, max(r, 32))
+               for (_, N, K, _, _, r) in layers)
+    wsp = torch.zeros(max(need, 256), dtype=torch.uint8, device="cuda")
+    return layers, ec_layers, xs, ys, wsp
+
+
+SLO_KINDS = (("attn", ("q", "k", "v", "o")), ("up", ("gate", "up")), ("down", ("down",)))
+SLO_GRID = (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096)
+
+
+def run_slo(args, torch, sp, gen):
+    """Latency table of the C5 stack's linear kinds, then the chunking trace."""
+    from quantized_gemm_w4a16_amd import chunking
+    layers, ec_layers, xs, ys, wsp = c5_stack(torch, sp, gen, max(SLO_GRID))
+    kinds, counts, table = [], [], []
+    for name, lins in SLO_KINDS:
+        for use_ec in (0, 1):
+            calls = [(N, K, w, ec) for (lin, N, K, w, ec, r) in layers
+                     if lin in lins and (ec is not None) == bool(use_ec)]
+            row = []
+            for M in SLO_GRID:
+                def record(n, calls=calls, M=M):
+                    for _ in range(n):
+                        for (N, K, w, ec) in calls:
+                            sp.spear_w4_linear(xs[K][:M], w, ec, y=ys[N][:M], workspace=wsp)
+                record(1)
+                torch.cuda.synchronize()
+                t = time_graph(torch, record, 2, 3)
+                row.append(t["median"] * 1e3 / len(calls))          # us per call
+            kinds.append(f"{name}{'_ec' if use_ec else ''}")
+            counts.append(len(calls))
+            table.append(row)
+    assert sp.spear_workspace_timeouts(wsp) == 0
+    lut = sp.SloLut(SLO_GRID, table, counts, 0.0)
+    trace = chunking.make_trace(gen.SEED_BASE + 7, 300, mean_gap_us=12000.0)
+    n_ref = 16
+    out_slo = []
+    for extra in (256, 1024):
+        slo = lut.predict(n_ref + extra)
+        res = [chunking.simulate(trace, lut, pol, slo, align=16).summary(slo)
+               for pol in ("dynamic", "static:256", "static:1024", "static:4096")]
+        out_slo.append({"slo_ms": round(slo / 1e3, 4),
+                        "slo_reading": f"predicted step of {n_ref} decode + {extra} prefill tokens",
+                        "policies": res})
+    # EC-aware: the chunk the picker allows at the tight objective as EC density grows
+    by_density = {}
+    slo = out_slo[0]["slo_ms"] * 1e3
+    for n_ec in (0, 4, 8, 16, 28):
+        cnt = []
+        for k in kinds:
+            per_layer = {"attn": 4, "up": 2, "down": 1}[k.split("_")[0]]
+            cnt.append(per_layer * (n_ec if k.endswith("_ec") else gen.C5_LAYERS - n_ec))
+        L = sp.SloLut(SLO_GRID, table, cnt, 0.0)
+        by_density[str(n_ec)] = L.pick_chunk(n_ref, 4096, slo, 16)[0]
+    lut_json = {"tokens": list(SLO_GRID), "kinds": kinds, "us_per_call": table,
+                "calls_per_step": counts,
+                "source": "measured by bench.py --workload slo: median of 3 replays of a "
+                          "graph over every call of the kind in the C5 stack"}
+    if args.lut_out:
+        with open(args.lut_out, "w") as f:
+            json.dump(lut_json, f, indent=1)
+    dyn = out_slo[0]["policies"][0]
+    return {
+        "metric": METRIC, "value": dyn["decode_tokens_per_s"], "unit": "decode tokens/s",
+        "n_gpus": 1, "steps": 2, "warmup": 1, "ms_per_step": None, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "EC-aware prefill chunking on the C5 stack (28 layers, ECs "
+                               f"on layers {sorted(ec_layers)}): latency table measured here, "
+                               "300 seeded requests (Poisson arrivals, mean gap 12 ms, "
+                               "log-normal prompts 64..4096, outputs 32..256)"},
+        "lut": lut_json, "slo": out_slo, "chunk_at_tight_slo_by_ec_layers": by_density,
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -566,7 +666,8 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     sp.load()
-    run = {"c1": run_c1, "c2": run_c2, "c3": run_c3, "c4": run_c4, "c5": run_c5}[args.workload]
+    run = {"c1": run_c1, "c2": run_c2, "c3": run_c3, "c4": run_c4, "c5": run_c5,
+           "slo": run_slo}[args.workload]
     out = run(args, torch, sp, gen)
     if args.copy_calibration:
         out["copy_calibration_bytes"] = copy_calibration(torch)

@@ -269,6 +269,47 @@ void spear_set_wait_limit(uint32_t rounds);
 spear_status spear_workspace_timeouts(void *workspace, int32_t *host_count, void *stream);
 
 /*
+ * EC-aware prefill chunking under an inter-token-latency objective (host
+ * only, no HIP call; all pointers are HOST pointers).  Source: the summary's
+ * section 2.2 C -- the scheduler takes the largest prefill chunk whose
+ * predicted inter-token latency meets the objective, from kernel-latency
+ * tables computed ahead of time, and adapts to how many layers carry ECs --
+ * and section 3.2 (stable latency objectives with dynamic chunking).
+ *
+ * The table holds, for each kind of linear call (a weight shape with or
+ * without its EC), the measured time of one call at a grid of token counts,
+ * and how many calls of that kind one forward step of the model makes (EC
+ * density enters through these counts).  One step over m tokens is predicted
+ * as overhead_us + sum_k count[k] L_k(m), with L_k the running maximum of the
+ * kind's measurements (so the prediction never falls as m grows), linear
+ * between grid points, its first value below the grid and its last segment's
+ * slope above it.
+ */
+typedef struct spear_lut {
+    int32_t npoints;        /* grid points, >= 1                                   */
+    const int32_t *tokens;  /* [npoints] token counts, ascending, tokens[0] >= 1   */
+    int32_t nkinds;         /* kinds of linear call, >= 1                          */
+    const float *us;        /* [nkinds][npoints] microseconds per call, finite, >= 0 */
+    const int32_t *count;   /* [nkinds] calls of each kind per step, >= 0          */
+    float overhead_us;      /* fixed time per step outside these calls, >= 0      */
+} spear_lut;
+
+/* Predicted time of one step over `tokens` tokens (0 for no tokens). */
+spear_status spear_slo_predict(const spear_lut *lut, int32_t tokens, float *us_out);
+
+/*
+ * spear_slo_pick_chunk -- the prefill chunk for the next step: the largest c,
+ * either `pending` itself or a multiple of `align` below it, such that a step
+ * over n_decode + c tokens (the running requests' decode tokens plus the
+ * chunk) is predicted within slo_us.  0 when even the smallest chunk does not
+ * fit.  *predicted_us (optional) receives the prediction for the chosen c.
+ *   n_decode >= 0, pending >= 0 (prompt tokens waiting), align >= 1.
+ */
+spear_status spear_slo_pick_chunk(const spear_lut *lut, int32_t n_decode, int32_t pending,
+                                  int32_t align, float slo_us, int32_t *chunk,
+                                  float *predicted_us);
+
+/*
  * spear_stream_read -- measurement helper, not part of the layer: reads every
  * byte of buf once (16-byte loads, four a thread in flight) and writes
  * nothing to *sink in practice (it is written only if the XOR of the data

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libspear.so")
-SOURCES = ["api.hip", "pack_gate.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.hip", "pack_gate.hip", "decode.hip", "prefill.hip", "slo.cpp"]
 ARCH = "gfx950"
 # Packed fp32 arithmetic is left to nothing: it is disabled for all device code.
 # The atomic optimizer turns a one-lane atomic with a uniform address into a

@@ -35,7 +35,8 @@ EXPORTS = ("spear_pack_w4", "spear_gate", "spear_w4_linear_workspace_size",
            "spear_workspace_init", "spear_w4_linear", "spear_w4_linear_path",
            "spear_w4_linear_noalloc",
            "spear_set_wait_limit", "spear_workspace_timeouts", "spear_stream_read",
-           "spear_status_string", "spear_abi_version")
+           "spear_slo_predict", "spear_slo_pick_chunk", "spear_status_string",
+           "spear_abi_version")
 
 
 class SpearError(RuntimeError):
@@ -57,6 +58,12 @@ class _EC(ctypes.Structure):
                 ("alpha", ctypes.c_float), ("gate_w1", ctypes.c_void_p),
                 ("gate_c1", ctypes.c_void_p), ("gate_w2", ctypes.c_void_p),
                 ("gate_c2", ctypes.c_void_p)]
+
+
+class _LUT(ctypes.Structure):
+    _fields_ = [("npoints", ctypes.c_int32), ("tokens", ctypes.c_void_p),
+                ("nkinds", ctypes.c_int32), ("us", ctypes.c_void_p), ("count", ctypes.c_void_p),
+                ("overhead_us", ctypes.c_float)]
 
 
 _lib = None
@@ -86,12 +93,15 @@ def load():
     lib.spear_set_wait_limit.restype = None
     lib.spear_workspace_timeouts.argtypes = [P, ctypes.POINTER(i32), P]
     lib.spear_stream_read.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.spear_slo_predict.argtypes = [ctypes.POINTER(_LUT), i32, ctypes.POINTER(ctypes.c_float)]
+    lib.spear_slo_pick_chunk.argtypes = [ctypes.POINTER(_LUT), i32, i32, i32, ctypes.c_float,
+                                         ctypes.POINTER(i32), ctypes.POINTER(ctypes.c_float)]
     lib.spear_status_string.argtypes = [i32]
     lib.spear_status_string.restype = ctypes.c_char_p
     lib.spear_abi_version.restype = i32
     for name in ("spear_pack_w4", "spear_gate", "spear_workspace_init", "spear_w4_linear",
                  "spear_w4_linear_path", "spear_w4_linear_noalloc", "spear_workspace_timeouts",
-                 "spear_stream_read"):
+                 "spear_stream_read", "spear_slo_predict", "spear_slo_pick_chunk"):
         getattr(lib, name).restype = i32
     _lib = lib
     return lib
@@ -268,3 +278,31 @@ def spear_stream_read(buf: torch.Tensor, sink: torch.Tensor, nbytes: Optional[in
     n = buf.numel() * buf.element_size() if nbytes is None else nbytes
     _check("spear_stream_read", load().spear_stream_read(_ptr(buf), n, _ptr(sink),
                                                          _stream(stream)))
+
+
+class SloLut:
+    """Kernel-latency table for the chunk picker (host memory): tokens [P]
+    ascending, us [kinds][P] microseconds per call, count [kinds] calls per
+    step, overhead_us per step."""
+
+    def __init__(self, tokens, us, count, overhead_us=0.0):
+        import numpy as np
+        self.tokens = np.ascontiguousarray(tokens, dtype=np.int32)
+        self.us = np.ascontiguousarray(us, dtype=np.float32)
+        self.count = np.ascontiguousarray(count, dtype=np.int32)
+        assert self.us.shape == (self.count.shape[0], self.tokens.shape[0])
+        self._c = _LUT(self.tokens.shape[0], self.tokens.ctypes.data, self.count.shape[0],
+                       self.us.ctypes.data, self.count.ctypes.data, float(overhead_us))
+
+    def predict(self, tokens: int) -> float:
+        out = ctypes.c_float(0)
+        _check("spear_slo_predict", load().spear_slo_predict(ctypes.byref(self._c), int(tokens),
+                                                             ctypes.byref(out)))
+        return float(out.value)
+
+    def pick_chunk(self, n_decode: int, pending: int, slo_us: float, align: int = 1):
+        c, p = ctypes.c_int32(0), ctypes.c_float(0)
+        _check("spear_slo_pick_chunk", load().spear_slo_pick_chunk(
+            ctypes.byref(self._c), int(n_decode), int(pending), int(align), float(slo_us),
+            ctypes.byref(c), ctypes.byref(p)))
+        return int(c.value), float(p.value)
