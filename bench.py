@@ -338,23 +338,30 @@ def measure_c4(args, torch, sp, gen, steps):
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     wsp = sp.new_workspace(M, N, K, r)
 
-    def steps_fn(use_ec):
+    sf = sp.SemiFused()
+
+    def steps_fn(use_ec, semi=False):
         def record(n):
             for i in range(n):
-                sp.spear_w4_linear(x, ws[i % R], ecs[i % R] if use_ec else None, y=y,
-                                   workspace=wsp)
+                if semi:
+                    sp.spear_w4_linear_semifused(x, ws[i % R], ecs[i % R], sf, y=y, workspace=wsp)
+                else:
+                    sp.spear_w4_linear(x, ws[i % R], ecs[i % R] if use_ec else None, y=y,
+                                       workspace=wsp)
         return record
 
     for _ in range(args.warmup):
         steps_fn(True)(1)
+        steps_fn(True, True)(1)
     torch.cuda.synchronize()
     t_ec = time_graph(torch, steps_fn(True), steps, args.replays)
     t_plain = time_graph(torch, steps_fn(False), steps, args.replays)
+    t_semi = time_graph(torch, steps_fn(True, True), steps, args.replays)
     assert sp.spear_workspace_timeouts(wsp) == 0
     flops = 2.0 * M * N * K
     ec_flops = 2.0 * M * K * r + 2.0 * M * r * N
     return {"M": M, "N": N, "K": K, "r": r, "flops": flops, "ec_flops": ec_flops,
-            "t_ec": t_ec, "t_plain": t_plain}
+            "t_ec": t_ec, "t_plain": t_plain, "t_semi": t_semi}
 
 
 def prefill_object(args, torch, sp, gen):
@@ -368,6 +375,11 @@ def prefill_object(args, torch, sp, gen):
            "ms_per_call": round(ms, 5), "plain_ms_per_call": round(ms0, 5),
            "ec_overhead": round(ms / ms0 - 1.0, 4),
            "timing": stats_ms(m["t_ec"], 5), "plain_timing": stats_ms(m["t_plain"], 5),
+           "semifused": {"what": "EC as a separate kernel on a second stream beside the plain "
+                                 "GEMM, joined by events (the pages' prefill form)",
+                         "ms_per_call": round(m["t_semi"]["median"], 5),
+                         "ec_overhead": round(m["t_semi"]["median"] / ms0 - 1.0, 4),
+                         "timing": stats_ms(m["t_semi"], 5)},
            "roofline": {"bound": "mfma", "achieved": round(tf0, 2), "peak": BF16_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tf0 / BF16_PEAK_TFLOPS, 4),
                         "traffic": None,
@@ -391,6 +403,8 @@ def run_c4(args, torch, sp, gen):
                                "Student-t(4) activations, EC rank 32 soft gate, fp32 output"},
         "timing": stats_ms(m["t_ec"]),
         "ec_overhead": round(ms / ms0 - 1.0, 4),
+        "semifused_ms_per_call": round(m["t_semi"]["median"], 6),
+        "semifused_ec_overhead": round(m["t_semi"]["median"] / ms0 - 1.0, 4),
         "plain_TFLOPs": round(tf0, 2),
         "plain_timing": stats_ms(m["t_plain"]),
         "roofline": {"bound": "mfma", "achieved": round(tf0, 2), "peak": BF16_PEAK_TFLOPS,
@@ -456,19 +470,25 @@ def run_c3(args, torch, sp, gen):
     x = dev(d["x"], torch)
     y = torch.empty((M, N), dtype=torch.float32, device="cuda")
     wsp = sp.new_workspace(M, N, K, r)
+    sf = sp.SemiFused()
 
-    def steps_fn(use_ec):
+    def steps_fn(use_ec, semi=False):
         def record(n):
             for i in range(n):
-                sp.spear_w4_linear(x, ws[i % R], ecs[i % R] if use_ec else None, y=y,
-                                   workspace=wsp)
+                if semi:
+                    sp.spear_w4_linear_semifused(x, ws[i % R], ecs[i % R], sf, y=y, workspace=wsp)
+                else:
+                    sp.spear_w4_linear(x, ws[i % R], ecs[i % R] if use_ec else None, y=y,
+                                       workspace=wsp)
         return record
 
     for _ in range(args.warmup):
         steps_fn(True)(1)
+        steps_fn(True, True)(1)
     torch.cuda.synchronize()
     t_ec = time_graph(torch, steps_fn(True), args.steps, args.replays)["median"] * args.steps
     t_plain = time_graph(torch, steps_fn(False), args.steps, args.replays)["median"] * args.steps
+    t_semi = time_graph(torch, steps_fn(True, True), args.steps, args.replays)["median"] * args.steps
     w, ecb, io = layer_bytes(M, N, K, r, True)
     ms = t_ec / args.steps
     gbs = (w + ecb + io) / (ms * 1e-3) / 1e9
@@ -484,6 +504,7 @@ def run_c3(args, torch, sp, gen):
                    "rotating_weight_copies": R},
         "TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
         "ec_overhead": round(t_ec / t_plain - 1.0, 4),
+        "semifused_ec_overhead": round(t_semi / t_plain - 1.0, 4),
         "plain_GBps": round((w + io) / (t_plain / args.steps * 1e-3) / 1e9, 2),
         "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,

@@ -224,6 +224,29 @@ spear_status spear_w4_linear_path(const spear_bf16 *x, int64_t M, const spear_w4
                                   void *workspace, size_t ws_bytes, int32_t path,
                                   void *stream);
 
+/*
+ * spear_w4_linear_semifused -- the prefill layer in the summary's semi-fused
+ * form (section 2.2 A: at prefill the EC runs as a separate kernel beside the
+ * low-bit GEMM, the two joined through the graph of the step).  On
+ * `aux_stream`, forked from `stream` by ev_fork: the EC pre-pass (gate logit,
+ * selection, v = g u, vector gate) and a ballot compaction of the active
+ * tokens.  On `stream`, meanwhile: the plain W4 GEMM into y.  Then `stream`
+ * waits for ev_join (recorded on aux_stream after the compaction) and one
+ * more kernel adds B v into the rows of the active tokens only.  No kernel
+ * waits on another stream's kernel; the fork and the join are event
+ * dependencies, which HIP graph capture of `stream` records as graph edges.
+ *   Arguments as for spear_w4_linear, except: y is fp32 only ([M][N]); ec may
+ *   be NULL (then: the plain GEMM on `stream`, nothing on aux_stream);
+ *   aux_stream is a stream other than `stream`; ev_fork and ev_join are
+ *   hipEvent_t handles owned by the caller (created with timing disabled is
+ *   enough), not used concurrently by other calls.  The workspace is that of
+ *   spear_w4_linear (spear_w4_linear_workspace_size).
+ */
+spear_status spear_w4_linear_semifused(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                       const spear_ec *ec, float *y, void *workspace,
+                                       size_t ws_bytes, void *stream, void *aux_stream,
+                                       void *ev_fork, void *ev_join);
+
 /* Size of the library's own scratch used by spear_w4_linear_noalloc, per GPU. */
 #define SPEAR_NOALLOC_MAX_WORKSPACE ((size_t)48 << 20)
 

@@ -146,6 +146,8 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
         off = align256(off + (size_t)(mt * L.rpad) * sizeof(uint64_t));
         L.active = off;
         off = align256(off + (size_t)L.mpad * 4);
+        L.idx = off;                                      // token list, then its count
+        off = align256(off + (size_t)(L.mpad + 1) * 4);
         // EC pre-pass with K split over workgroups: per-slot partials as tagged
         // 64-bit words (sized independently of M).
         L.preu = off;
@@ -380,25 +382,12 @@ static spear_status validate_linear(const spear_bf16 *x, int64_t M, const spear_
     return SPEAR_OK;
 }
 
-// A validated layer call: dispatch and launch on `stream`.
-static spear_status run_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,
-                               const spear_ec *ec, void *y, int32_t out_dtype, void *workspace,
-                               int32_t path, void *stream)
+// The kernel arguments of a validated call.
+static void fill_args(LinearArgs &a, const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                      const spear_ec *ec, void *y, int32_t out_dtype, void *workspace,
+                      int32_t path, const WsLayout &L)
 {
     const int64_t N = w->N, K = w->K;
-    const WsLayout L = ws_layout(M, N, K, ec ? ec->r : 0);
-    spear_status st = check_device();
-    if (st != SPEAR_OK)
-        return st;
-    hipStream_t s = (hipStream_t)stream;
-
-    if (M == 0) {
-        if (ec && ec->n_active_out)
-            return hip_status(launch_zero(ec->n_active_out, sizeof(int32_t), s));
-        return SPEAR_OK;
-    }
-
-    LinearArgs a;
     memset(&a, 0, sizeof a);
     a.x = x;
     a.packed = w->packed;
@@ -456,8 +445,14 @@ static spear_status run_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w
         }
     }
 
+}
+
+// The launches of one path.
+static spear_status launch_path(LinearArgs &a, const spear_ec *ec, int32_t path, hipStream_t s)
+{
+    const int64_t M = a.M, N = a.N, K = a.K;
     hipError_t e = hipSuccess;
-    const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + L.active);
+    const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
     switch (path) {
     case SPEAR_PATH_DECODE:
         if (!(ec && ec->gate_h > 0 && a.rpad > 32)) {
@@ -507,6 +502,30 @@ static spear_status run_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w
     }
     return hip_status(e);
 }
+
+// A validated layer call: dispatch and launch on `stream`.
+static spear_status run_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                               const spear_ec *ec, void *y, int32_t out_dtype, void *workspace,
+                               int32_t path, void *stream)
+{
+    const int64_t N = w->N, K = w->K;
+    const WsLayout L = ws_layout(M, N, K, ec ? ec->r : 0);
+    spear_status st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (M == 0) {
+        if (ec && ec->n_active_out)
+            return hip_status(launch_zero(ec->n_active_out, sizeof(int32_t), s));
+        return SPEAR_OK;
+    }
+
+    LinearArgs a;
+    fill_args(a, x, M, w, ec, y, out_dtype, workspace, path, L);
+    return launch_path(a, ec, path, s);
+}
+
 
 // Scratch of the allocation-free entry point: one copy per GPU, zero at load
 // (static storage), held until the process ends.  In host code `scratch`
@@ -563,6 +582,52 @@ spear_status spear_w4_linear_noalloc(const spear_bf16 *x, int64_t M, const spear
     if (st != SPEAR_OK)
         return st;
     return run_linear(x, M, w, ec, y, out_dtype, ws, path, stream);
+}
+
+spear_status spear_w4_linear_semifused(const spear_bf16 *x, int64_t M, const spear_w4 *w,
+                                       const spear_ec *ec, float *y, void *workspace,
+                                       size_t ws_bytes, void *stream, void *aux_stream,
+                                       void *ev_fork, void *ev_join)
+{
+    int32_t path = SPEAR_PATH_PREFILL;
+    spear_status st = validate_linear(x, M, w, ec, y, SPEAR_OUT_F32, workspace, ws_bytes, &path);
+    if (st != SPEAR_OK)
+        return st;
+    if (ec && (!ev_fork || !ev_join))
+        return SPEAR_E_NULL;
+    if (ec && aux_stream == stream)
+        return SPEAR_E_ARG;
+    if (!ec || M == 0)
+        return run_linear(x, M, w, ec, y, SPEAR_OUT_F32, workspace, path, stream);
+    st = check_device();
+    if (st != SPEAR_OK)
+        return st;
+    const WsLayout L = ws_layout(M, w->N, w->K, ec->r);
+    LinearArgs a;
+    fill_args(a, x, M, w, ec, y, SPEAR_OUT_F32, workspace, path, L);
+    hipStream_t s = (hipStream_t)stream, s2 = (hipStream_t)aux_stream;
+    hipEvent_t e0 = (hipEvent_t)ev_fork, e1 = (hipEvent_t)ev_join;
+    int32_t *active = reinterpret_cast<int32_t *>(a.ws + L.active);
+    int32_t *list = reinterpret_cast<int32_t *>(a.ws + L.idx);
+    // fork: the EC branch on the auxiliary stream
+    hipError_t e = hipEventRecord(e0, s);
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(s2, e0, 0);
+    if (e == hipSuccess)
+        e = launch_prepass(a, s2);
+    if (e == hipSuccess)
+        e = launch_compact(active, M, list, list + L.mpad, s2, a.idx_out, a.nact_out);
+    if (e == hipSuccess)
+        e = hipEventRecord(e1, s2);
+    // the plain W4 GEMM on the caller's stream, beside it
+    if (e == hipSuccess)
+        e = launch_gemm(a, 0, 0, s);
+    // join, then the EC kernel over the active tokens
+    if (e == hipSuccess)
+        e = hipStreamWaitEvent(s, e1, 0);
+    if (e == hipSuccess)
+        e = launch_ec_apply(a, s);
+    return hip_status(e);
 }
 
 spear_status spear_w4_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,

@@ -105,9 +105,11 @@ __global__ __launch_bounds__(256) void gate_kernel(const uint16_t *__restrict__ 
 // alias idx: a chunk's flags are all read before any of its indices is written,
 // and every write lands below the next chunk.  idx may be NULL (count only).
 // A negative flag marks a token whose gate is unknown (an expired wait
-// upstream); the count is then -1.
+// upstream); the count is then -1.  A second destination (idx2, nact2) may
+// receive the same list.
 __global__ __launch_bounds__(1024) void compact_kernel(const int32_t *flags, int64_t M,
-                                                       int32_t *idx, int32_t *nact)
+                                                       int32_t *idx, int32_t *nact, int32_t *idx2,
+                                                       int32_t *nact2)
 {
     __shared__ int wave_tot[16];
     __shared__ int any_bad;
@@ -135,11 +137,15 @@ __global__ __launch_bounds__(1024) void compact_kernel(const int32_t *flags, int
         }
         if (f && idx)
             idx[off + __popcll(mask & ((1ull << lane) - 1ull))] = (int32_t)i;
+        if (f && idx2)
+            idx2[off + __popcll(mask & ((1ull << lane) - 1ull))] = (int32_t)i;
         base += total;
         __syncthreads();
     }
     if (tid == 0 && nact)
         *nact = any_bad ? -1 : (int32_t)base;
+    if (tid == 0 && nact2)
+        *nact2 = any_bad ? -1 : (int32_t)base;
 }
 
 hipError_t launch_gate(const uint16_t *x, int64_t M, int64_t K, const uint16_t *wg, float b,
@@ -157,9 +163,9 @@ hipError_t launch_gate(const uint16_t *x, int64_t M, int64_t K, const uint16_t *
 }
 
 hipError_t launch_compact(const int32_t *flags, int64_t M, int32_t *idx, int32_t *nact,
-                          hipStream_t s)
+                          hipStream_t s, int32_t *idx2, int32_t *nact2)
 {
-    hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, flags, M, idx, nact);
+    hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, flags, M, idx, nact, idx2, nact2);
     return hipGetLastError();
 }
 

@@ -1308,7 +1308,85 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ EC apply kernel
+// The separate EC kernel of the semi-fused prefill (summary section 2.2 A: at
+// prefill the EC runs as its own kernel beside the GEMM, joined through the
+// graph), after the join: y[m][n] += sum_j B[n][j] v[m][j] for the active
+// tokens only, taken from the compacted list (ascending indices, then their
+// count), so that tokens the hard gate skips cost no work and no traffic.
+// v = g (alpha gamma) u is the pre-pass's, as bf16 hi + lo.  A workgroup takes
+// 16 listed tokens x 256 channels (4 waves of 64): 16 x 16 MFMA tiles with
+// the channels as rows, the tokens as columns, 32 ranks deep, then
+// read-add-write of y (fp32).  A count of -1 (an expired wait in the
+// pre-pass) walks every token instead and writes NaN where the selection
+// flag is -1.
+__global__ __launch_bounds__(256) void ec_apply_kernel(const LinearArgs a)
+{
+    const int64_t M = a.M, N = a.N;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int32_t *list = reinterpret_cast<const int32_t *>(a.ws + a.L.idx);
+    const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
+    const int32_t nact = list[a.mpad];
+    const bool bad = nact < 0;
+    const int64_t cnt = bad ? M : nact;
+    const int64_t t0 = (int64_t)blockIdx.x * 16;
+    if (t0 >= cnt)
+        return;
+    const int64_t slot = t0 + lr;
+    int64_t m = -1;                                   // the token of column lr
+    if (slot < cnt)
+        m = bad ? slot : list[slot];
+    const int flag = m >= 0 ? active[m] : 0;
+    const bool use = m >= 0 && flag != 0;
+    const int64_t n0 = (int64_t)blockIdx.y * 256 + 64 * wave;
+    const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
+    const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
+    const int rpad = a.rpad, r = a.r;
+    f32x4 acc[4];
+#pragma unroll
+    for (int fn = 0; fn < 4; fn++)
+        acc[fn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < rpad / 32; t++) {
+        const int j = 32 * t + 8 * lg;
+        const u32x4 vh = use ? ld16(vhi + m * rpad + j) : zero4();
+        const u32x4 vl = use ? ld16(vlo + m * rpad + j) : zero4();
+#pragma unroll
+        for (int fn = 0; fn < 4; fn++) {
+            const int64_t n = n0 + 16 * fn + lr;
+            const u32x4 bf = (n < N && j < r) ? ld16(a.B + n * r + j) : zero4();
+            acc[fn] = mfma16(bf, vh, acc[fn]);
+            acc[fn] = mfma16(bf, vl, acc[fn]);
+        }
+    }
+    // lane (lr, lg) holds channels n0 + 16 fn + 4 lg + i of token m
+    if (!use)
+        return;
+    float *yr = reinterpret_cast<float *>(a.y) + m * N;
+    const float qnan = __builtin_nanf("");
+#pragma unroll
+    for (int fn = 0; fn < 4; fn++) {
+        const int64_t nb = n0 + 16 * fn + 4 * lg;
+        if (nb + 3 < N && (N & 3) == 0) {
+            f32x4 v = *reinterpret_cast<const f32x4 *>(yr + nb);
+            v = flag < 0 ? f32x4{qnan, qnan, qnan, qnan} : v + acc[fn];
+            *reinterpret_cast<f32x4 *>(yr + nb) = v;
+        } else {
+            for (int i = 0; i < 4; i++)
+                if (nb + i < N)
+                    yr[nb + i] = flag < 0 ? qnan : yr[nb + i] + acc[fn][i];
+        }
+    }
+}
+
 } // namespace
+
+hipError_t launch_ec_apply(const LinearArgs &a, hipStream_t s)
+{
+    const dim3 grid((unsigned)((a.M + 15) / 16), (unsigned)((a.N + 255) / 256));
+    hipLaunchKernelGGL(ec_apply_kernel, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 {

@@ -136,6 +136,7 @@ constexpr int PRE_GROUPS = 128;   // EC pre-pass: token groups below which K is 
 
 struct WsLayout {
     size_t hdr, epoch, zeros, splitp, pu, pz, vhi, vlo, vtag, active, preu, prez, gpart, total;
+    size_t idx;         // semi-fused prefill: the active-token list [mpad], then its count
     int64_t ncg, ksplit, spw, nprod, prod_k, rpad, mpad;
 };
 
@@ -206,7 +207,7 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
     pin_arg(a.pre_ks); pin_arg(a.g_ks); pin_arg(a.g_bn); pin_arg(a.npre); pin_arg(a.L.vtag); pin_arg(a.L.gpart); pin_arg(a.L.preu); pin_arg(a.L.prez);
     pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.splitp); pin_arg(a.L.pu);
-    pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active);
+    pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active); pin_arg(a.L.idx);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);
     pin_arg(a.gw1); pin_arg(a.gc1); pin_arg(a.gw2); pin_arg(a.gc2); pin_arg(a.gate_h); pin_arg(a.alpha);
 }
@@ -265,11 +266,12 @@ hipError_t launch_gate(const uint16_t *x, int64_t M, int64_t K, const uint16_t *
                        double thr, int32_t hard, float *g, int32_t *idx, int32_t *nact,
                        hipStream_t s);
 hipError_t launch_compact(const int32_t *flags, int64_t M, int32_t *idx, int32_t *nact,
-                          hipStream_t s);
+                          hipStream_t s, int32_t *idx2 = nullptr, int32_t *nact2 = nullptr);
 hipError_t launch_zero(void *p, size_t bytes, hipStream_t s);
 hipError_t launch_stream_read(const void *p, size_t bytes, uint32_t *sink, hipStream_t s);
 hipError_t launch_decode(const LinearArgs &a, int ec_mode, hipStream_t s);
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s);
 hipError_t launch_gemm(const LinearArgs &a, int ec_on, int force_large, hipStream_t s);
+hipError_t launch_ec_apply(const LinearArgs &a, hipStream_t s);
 
 } // namespace spear

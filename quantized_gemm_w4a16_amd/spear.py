@@ -33,7 +33,7 @@ ABI_VERSION = 2
 
 EXPORTS = ("spear_pack_w4", "spear_gate", "spear_w4_linear_workspace_size",
            "spear_workspace_init", "spear_w4_linear", "spear_w4_linear_path",
-           "spear_w4_linear_noalloc",
+           "spear_w4_linear_noalloc", "spear_w4_linear_semifused",
            "spear_set_wait_limit", "spear_workspace_timeouts", "spear_stream_read",
            "spear_slo_predict", "spear_slo_pick_chunk", "spear_status_string",
            "spear_abi_version")
@@ -89,6 +89,8 @@ def load():
     lib.spear_w4_linear_path.argtypes = lin + [i32, P]
     lib.spear_w4_linear_noalloc.argtypes = [P, i64, ctypes.POINTER(_W4), ctypes.POINTER(_EC), P,
                                             i32, i32, P]
+    lib.spear_w4_linear_semifused.argtypes = [P, i64, ctypes.POINTER(_W4), ctypes.POINTER(_EC), P,
+                                              P, ctypes.c_size_t, P, P, P, P]
     lib.spear_set_wait_limit.argtypes = [ctypes.c_uint32]
     lib.spear_set_wait_limit.restype = None
     lib.spear_workspace_timeouts.argtypes = [P, ctypes.POINTER(i32), P]
@@ -100,7 +102,8 @@ def load():
     lib.spear_status_string.restype = ctypes.c_char_p
     lib.spear_abi_version.restype = i32
     for name in ("spear_pack_w4", "spear_gate", "spear_workspace_init", "spear_w4_linear",
-                 "spear_w4_linear_path", "spear_w4_linear_noalloc", "spear_workspace_timeouts",
+                 "spear_w4_linear_path", "spear_w4_linear_noalloc", "spear_w4_linear_semifused",
+                 "spear_workspace_timeouts",
                  "spear_stream_read", "spear_slo_predict", "spear_slo_pick_chunk"):
         getattr(lib, name).restype = i32
     _lib = lib
@@ -236,6 +239,40 @@ def spear_w4_linear(x: torch.Tensor, w: W4, ec: Optional[EC] = None,
                                      _ptr(y), out_dtype, _ptr(workspace), workspace.numel(),
                                      path, _stream(stream))
     _check("spear_w4_linear", st)
+    return y
+
+
+class SemiFused:
+    """The second stream and the two events of the semi-fused prefill (torch
+    objects; the events are recorded once so that their HIP handles exist)."""
+
+    def __init__(self, device="cuda"):
+        self.aux = torch.cuda.Stream(device=device)
+        self.ev_fork = torch.cuda.Event()
+        self.ev_join = torch.cuda.Event()
+        self.ev_fork.record(self.aux)
+        self.ev_join.record(self.aux)
+        self.aux.synchronize()
+
+
+def spear_w4_linear_semifused(x: torch.Tensor, w: W4, ec: Optional[EC], sf: SemiFused,
+                              y: Optional[torch.Tensor] = None,
+                              workspace: Optional[torch.Tensor] = None,
+                              stream=None) -> torch.Tensor:
+    """The prefill layer with the EC as a separate kernel on sf.aux (fp32 y)."""
+    M = int(x.shape[0])
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    if workspace is None:
+        workspace = new_workspace(M, w.N, w.K, ec.r if ec is not None else 0, x.device)
+    wc = w._c()
+    ecc = ec._c() if ec is not None else None
+    st = load().spear_w4_linear_semifused(_ptr(x), M, ctypes.byref(wc),
+                                          ctypes.byref(ecc) if ecc is not None else None,
+                                          _ptr(y), _ptr(workspace), workspace.numel(),
+                                          _stream(stream), sf.aux.cuda_stream,
+                                          sf.ev_fork.cuda_event, sf.ev_join.cuda_event)
+    _check("spear_w4_linear_semifused", st)
     return y
 
 
