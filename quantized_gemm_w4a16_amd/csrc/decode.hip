@@ -59,6 +59,7 @@ struct DecShared {
     float red[DEC_WAVES][64][5];
     alignas(16) float red16[DEC_WAVES][16];   // one token: each wave's channel sums
     float xs[DEC_WAVES];        // one token: the activation sum of each wave's chunks
+    double zl[DEC_WAVES];       // one token, hard gate: each wave's gate-logit partial
     uint32_t u32[4];
 };
 
@@ -613,6 +614,22 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
             *reinterpret_cast<u32x4 *>(s_x + M * rs_bytes + 16 * q) = zero4();
     }
 
+    // 3b. One token under the hard gate, with all of K in this workgroup: the
+    //     gate logit is formed here too, so that a token the gate skips takes
+    //     no EC exchange at all.  The wave loads the w_g chunks of its own
+    //     activation chunks before the weight stream, so the wait for the
+    //     activations below also covers them.  Every workgroup sums the same
+    //     products in the same order, so all agree on the selection.
+    constexpr int WGQ = (SW + 3) / 4;                        // chunks a lane takes: c1 - c0 <= 16 SW
+    const bool zloc = EC_MODE == 1 && GV && a.hard && ksplit == 1;
+    u32x4 wgv[WGQ];
+#pragma unroll
+    for (int i = 0; i < WGQ; i++) {
+        const int64_t q = c0 + lane + 64 * i;
+        const int64_t k = s_begin * 128 + 8 * q;
+        wgv[i] = (zloc && q < c1 && k < K) ? ld16(a.wg + k) : zero4();
+    }
+
     // 4. The weight stream of this wave: SW loads, all in flight at once.  Out of
     //    range rows and depths read clamped in-bounds addresses; their products
     //    meet zero activations or are never stored.
@@ -643,13 +660,29 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     //    order.  More tokens take their sums from a ones-MFMA in the loop.
     if (GV) {
         float xsum = 0.f;
-        for (int64_t q = c0 + lane; q < c1; q += 64)
-            xsum = sum8(*reinterpret_cast<const u32x4 *>(s_x + 16 * q), xsum);
+        double zp = 0.0;
+#pragma unroll
+        for (int i = 0; i < WGQ; i++) {
+            const int64_t q = c0 + lane + 64 * i;
+            if (q < c1) {
+                const u32x4 xv = *reinterpret_cast<const u32x4 *>(s_x + 16 * q);
+                xsum = sum8(xv, xsum);
+                if (zloc)
+                    zp = dot8_f64(xv, wgv[i], zp);
+            }
+        }
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1)
             xsum += __shfl_xor(xsum, o);
         if (lane == 0)
             sh.xs[wave] = xsum;
+        if (zloc) {
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1)
+                zp += __shfl_xor(zp, o);
+            if (lane == 0)
+                sh.zl[wave] = zp;
+        }
     }
 
     // 6. Contraction (stream waves), each super-step as soon as its weights land.
@@ -753,8 +786,25 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
             ec_e = ec_consume<8, (GV && 8 == 1)>(a, bpre, cg, wave, lane, s_x, tag, &ok, overlap);
     };
 
+    // A token the hard gate skips (logit formed in this workgroup): no EC
+    // exchange; the first channel group reports the gate.
+    bool skip_ec = false;
+    if (zloc) {
+        double z = (double)a.b;
+        for (int w = 0; w < DEC_WAVES; w++)
+            z += sh.zl[w];
+        if (!(z > a.thr)) {
+            skip_ec = true;
+            if (cg == 0 && tid == 0) {
+                if (a.g_out)
+                    a.g_out[0] = (float)(1.0 / (1.0 + exp(-z)));
+                if (a.nact_out)
+                    *a.nact_out = 0;
+            }
+        }
+    }
     bool epi = true;
-    if (EC_MODE == 1 && ksplit == 1) {
+    if (EC_MODE == 1 && ksplit == 1 && !skip_ec) {
         consume(reduce_waves);
     } else {
         reduce_waves();
@@ -834,7 +884,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
                 }
             }
         }
-        if (EC_MODE == 1 && epi)
+        if (EC_MODE == 1 && epi && !skip_ec)
             consume([] {});
     }
 

@@ -391,3 +391,50 @@ def test_c5_stack_layers_sampled(M):
             n = int(e.n_active_out.item())
             assert n == gref["n_active"]
             assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
+
+
+@pytest.mark.parametrize("K", [1056, 4096, 8192])
+@pytest.mark.parametrize("bias", [-4.0, 0.0, 4.0])
+def test_decode_one_token_hard_gate(K, bias):
+    """One token, hard gate: the stream workgroups form the gate logit
+    themselves (all of K in one workgroup) and a skipped token takes no EC
+    exchange; with K split over workgroups the producers' logit decides.  The
+    bias moves the token to either side of the threshold; the output, the gate
+    value and the selection match the oracle."""
+    d = random_case(1, 1000, K, 32, oracle.CODES_U4, 1, seed=900 + K)
+    d["ec"] = dict(d["ec"], b=bias)
+    gref = oracle.gate(d["x"], d["ec"]["w_g"], bias, d["ec"]["tau"], 1)
+    w = gpu_weights(d)
+    for path in (sp.PATH_DECODE, sp.PATH_DECODE_2PASS):
+        y, e = run_gpu(d, path=path, w=w)
+        assert_close(y, run_oracle(d), f"one token hard gate K={K} b={bias} path={path}")
+        n = int(e.n_active_out.item())
+        assert n == gref["n_active"]
+        assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
+        np.testing.assert_allclose(host(e.g_out)[:1], gref["g"], rtol=2e-7)
+    if gref["n_active"] == 0:
+        plain, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ec=False)
+        y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w)
+        assert np.array_equal(y, plain)
+
+
+@pytest.mark.parametrize("M", [2, 16])
+def test_decode_mixed_activity(M):
+    """Several tokens under the hard gate, some selected and some not (the
+    bias puts the threshold inside the tokens' logits): per-token EC terms,
+    the selection list and the count match the oracle on every decode path."""
+    d = random_case(M, 640, 2048, 32, oracle.CODES_S4, 1, seed=70 + M)
+    gref = oracle.gate(d["x"], d["ec"]["w_g"], d["ec"]["b"], d["ec"]["tau"], 1)
+    z = np.sort(gref["z"])
+    b = float(d["ec"]["b"] - (z[M // 2 - 1] + z[M // 2]) / 2)   # about half selected
+    d["ec"] = dict(d["ec"], b=b)
+    gref = oracle.gate(d["x"], d["ec"]["w_g"], b, d["ec"]["tau"], 1)
+    assert 0 < gref["n_active"] < M
+    ref = run_oracle(d)
+    w = gpu_weights(d)
+    for path in (sp.PATH_DECODE, sp.PATH_DECODE_2PASS, sp.PATH_PREFILL):
+        y, e = run_gpu(d, path=path, w=w)
+        assert_close(y, ref, f"mixed activity M={M} path={path}")
+        n = int(e.n_active_out.item())
+        assert n == gref["n_active"]
+        assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
