@@ -94,8 +94,9 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
     memset(&L, 0, sizeof L);
     L.ncg = cdiv(N, 16);
     // Decode: a workgroup stages the activations of its K range in LDS
-    // (M rows of 128-deep super-steps, 256 bytes each plus 16 of padding) and
-    // its 4 waves take at most DEC_SW_MAX super-steps each.
+    // (M rows of 128-deep super-steps, 256 bytes each plus 16 of padding); a
+    // range holds at most DEC_WAVES * DEC_SW_MAX super-steps, split over the
+    // workgroup's stream waves.
     const int64_t S = cdiv(K, 128);
     const int64_t mr = M < 1 ? 1 : (M > 16 ? 16 : M);
     int64_t smax = (DEC_LDS_MAX / (mr + 1) - 16) / 256;   // M + 1 rows (one of zeros)

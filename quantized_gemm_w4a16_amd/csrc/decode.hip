@@ -53,13 +53,21 @@ namespace spear {
 
 namespace {
 
-constexpr int DEC_THREADS = 64 * DEC_WAVES;               // stream waves
+// Stream waves of a workgroup: DEC_WAVES with the fused EC (its producers and
+// epilogue exchange are laid out for 4 waves), DEC_WAVES_PLAIN otherwise.  Eight
+// waves take half as many super-steps each and keep twice as many loads in
+// flight per CU (plain one-token C2 launch 5.5 -> 5.3 us, eight tokens 7.6 ->
+// 6.1 us).  The shared block is sized for the waves the kernel has: with the
+// fused EC, a producer must fit on a CU beside a stream workgroup that holds
+// nine token rows (2 x 79.3 KiB of LDS).
+constexpr int DEC_WAVES_PLAIN = 8;
 
+template <int NW>
 struct DecShared {
-    float red[DEC_WAVES][64][5];
-    alignas(16) float red16[DEC_WAVES][16];   // one token: each wave's channel sums
-    float xs[DEC_WAVES];        // one token: the activation sum of each wave's chunks
-    double zl[DEC_WAVES];       // one token, hard gate: each wave's gate-logit partial
+    float red[NW][64][5];
+    alignas(16) float red16[NW][16];   // one token: each wave's channel sums
+    float xs[NW];        // one token: the activation sum of each wave's chunks
+    double zl[NW];       // one token, hard gate: each wave's gate-logit partial
     uint32_t u32[4];
 };
 
@@ -525,10 +533,11 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
     return e * gs;
 }
 
-template <int EC_MODE, int OUT_F32, int SW, int GV>
-__global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs a)
+template <int EC_MODE, int OUT_F32, int SW, int GV, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
 {
-    __shared__ DecShared sh;
+    static_assert(EC_MODE != 1 || NW == DEC_WAVES, "the fused EC's exchange is laid out for 4 waves");
+    __shared__ DecShared<NW> sh;
     extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];
     pin_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -756,12 +765,12 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     float rst = 0.f;
     auto reduce_waves = [&]() {
         if (GV && wave == 0) {
-            for (int w = 0; w < DEC_WAVES; w++) {
+            for (int w = 0; w < NW; w++) {
                 tot += *reinterpret_cast<const f32x4 *>(&sh.red16[w][4 * lg]);
                 rst += sh.xs[w];
             }
         } else if (wave == 0) {
-            for (int w = 0; w < DEC_WAVES; w++) {
+            for (int w = 0; w < NW; w++) {
 #pragma unroll
                 for (int i = 0; i < 4; i++)
                     tot[i] += sh.red[w][lane][i];
@@ -791,7 +800,7 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
     bool skip_ec = false;
     if (zloc) {
         double z = (double)a.b;
-        for (int w = 0; w < DEC_WAVES; w++)
+        for (int w = 0; w < NW; w++)
             z += sh.zl[w];
         if (!(z > a.thr)) {
             skip_ec = true;
@@ -959,26 +968,30 @@ __global__ __launch_bounds__(64 * DEC_WAVES) void decode_kernel(const LinearArgs
 template <int EC_MODE, int OUT_F32, int SW, int GV>
 hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
 {
+    constexpr int NW = EC_MODE == 1 ? DEC_WAVES : DEC_WAVES_PLAIN;
     static const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_kernel<EC_MODE, OUT_F32, SW, GV>),
+        reinterpret_cast<const void *>(&decode_kernel<EC_MODE, OUT_F32, SW, GV, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, DEC_LDS_MAX);
     if (e != hipSuccess)
         return e;
     const int64_t npwg = EC_MODE == 1 ? a.nprod : 0;
     const dim3 grid((unsigned)(npwg + a.ncg * a.ksplit));
-    const dim3 block(64 * DEC_WAVES);
+    const dim3 block(64 * NW);
     size_t lds = (size_t)(a.M + 1) * (size_t)(a.spw * 256 + 16);
     const size_t ec_lds = EC_LDS + (a.gate_h > 0 ? EC_LDS_VG : 0);
     if (EC_MODE == 1 && lds < ec_lds)
         lds = ec_lds;                                     // EC partials meet in the same LDS
-    hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW, GV>), grid, block, lds, s, a);
+    hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW, GV, NW>), grid, block, lds, s, a);
     return hipGetLastError();
 }
 
+// SW = super-steps a stream wave takes: the workgroup's range split over its
+// waves (at most DEC_WAVES * DEC_SW_MAX super-steps, so SW <= DEC_SW_MAX).
 template <int EC_MODE, int OUT_F32, int GV>
 hipError_t launch_decode_sw(const LinearArgs &a, hipStream_t s)
 {
-    switch ((a.spw + DEC_WAVES - 1) / DEC_WAVES) {
+    constexpr int NW = EC_MODE == 1 ? DEC_WAVES : DEC_WAVES_PLAIN;
+    switch ((a.spw + NW - 1) / NW) {
     case 1: return launch_decode_k<EC_MODE, OUT_F32, 1, GV>(a, s);
     case 2: return launch_decode_k<EC_MODE, OUT_F32, 2, GV>(a, s);
     case 3: return launch_decode_k<EC_MODE, OUT_F32, 3, GV>(a, s);

@@ -11,8 +11,8 @@ import torch
 import oracle
 from quantized_gemm_w4a16_amd import inputs as gen
 from quantized_gemm_w4a16_amd import spear as sp
-from gpu_util import (assert_close, dev, errors, gpu_ec, gpu_weights, host, run_gpu,
-                      run_oracle)
+from gpu_util import (assert_close, assert_reordered, dev, errors, gpu_ec, gpu_weights, host,
+                      run_gpu, run_oracle)
 
 pytestmark = pytest.mark.gpu
 
@@ -224,15 +224,25 @@ def test_ragged_shapes(M, N, K, r, kind, hard):
                                     (sp.PATH_DECODE_2PASS, 8), (sp.PATH_PREFILL, 16),
                                     (sp.PATH_PREFILL, 150)])
 def test_invariants_bitwise(path, M):
-    """tau = 1, A = 0 and b = -inf each reduce the layer to plain W4 bit for bit;
-    repeated calls are bitwise identical (no floating-point atomics)."""
+    """tau = 1, A = 0 and b = -inf each make the EC term an exact zero: the three
+    outputs are bitwise identical, and bitwise equal to plain W4 where the plain
+    layer runs the same stream form (the two-pass decode and the prefill); the
+    fused decode streams with 4 waves against the plain decode's 8, so there
+    they agree to the rounding of the reordered sum.  Repeated calls are
+    bitwise identical (no floating-point atomics)."""
     d = random_case(M, 272, 1024, 32, oracle.CODES_U4, 0, seed=500 + M + path)
     w = gpu_weights(d)
     plain, _ = run_gpu(d, path=path, w=w, ec=False)
+    off = []
     for mod in [dict(hard=1, tau=1.0), dict(A=np.zeros_like(d["ec"]["A"])),
                 dict(b=-math.inf)]:
         y, _ = run_gpu(d, path=path, w=w, ec=dict(d["ec"], **mod))
-        assert np.array_equal(y, plain), mod
+        if path == sp.PATH_DECODE:
+            assert_reordered(y, plain, f"EC off {mod}")
+        else:
+            assert np.array_equal(y, plain), mod
+        off.append(y)
+    assert np.array_equal(off[0], off[1]) and np.array_equal(off[0], off[2])
     y1, _ = run_gpu(d, path=path, w=w)
     y2, _ = run_gpu(d, path=path, w=w)
     assert np.array_equal(y1, y2)
@@ -413,9 +423,16 @@ def test_decode_one_token_hard_gate(K, bias):
         assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
         np.testing.assert_allclose(host(e.g_out)[:1], gref["g"], rtol=2e-7)
     if gref["n_active"] == 0:
+        # the skipped token's output is the fused kernel's own W4 sum: bitwise
+        # that of a selected token whose EC term is an exact zero (A = 0), and
+        # the plain layer's up to the reordered sum
         plain, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ec=False)
         y, _ = run_gpu(d, path=sp.PATH_DECODE, w=w)
-        assert np.array_equal(y, plain)
+        zero_a = dict(d["ec"], A=np.zeros_like(d["ec"]["A"]), b=bias + 100.0)
+        y0, e0 = run_gpu(d, path=sp.PATH_DECODE, w=w, ec=zero_a)
+        assert int(e0.n_active_out.item()) == 1
+        assert np.array_equal(y, y0)
+        assert_reordered(y, plain, f"one token skipped K={K}")
 
 
 @pytest.mark.parametrize("M", [2, 16])
