@@ -54,13 +54,12 @@ namespace spear {
 namespace {
 
 // Stream waves of a workgroup: DEC_WAVES with the fused EC (its producers and
-// epilogue exchange are laid out for 4 waves), DEC_WAVES_PLAIN otherwise.  Eight
-// waves take half as many super-steps each and keep twice as many loads in
-// flight per CU (plain one-token C2 launch 5.5 -> 5.3 us, eight tokens 7.6 ->
-// 6.1 us).  The shared block is sized for the waves the kernel has: with the
-// fused EC, a producer must fit on a CU beside a stream workgroup that holds
-// nine token rows (2 x 79.3 KiB of LDS).
+// epilogue exchange are laid out for 4 waves); without it DEC_WAVES_PLAIN where
+// plain_waves picks it.  The shared block is sized for the waves the kernel
+// has: with the fused EC, a producer must fit on a CU beside a stream
+// workgroup that holds nine token rows (2 x 79.3 KiB of LDS).
 constexpr int DEC_WAVES_PLAIN = 8;
+constexpr int64_t DEC_CUS = 256;                            // compute units of the chip
 
 template <int NW>
 struct DecShared {
@@ -965,10 +964,9 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
 }
 
 // Dynamic LDS beyond 64 KiB must be enabled per kernel once.
-template <int EC_MODE, int OUT_F32, int SW, int GV>
+template <int EC_MODE, int OUT_F32, int SW, int GV, int NW>
 hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
 {
-    constexpr int NW = EC_MODE == 1 ? DEC_WAVES : DEC_WAVES_PLAIN;
     static const hipError_t e = hipFuncSetAttribute(
         reinterpret_cast<const void *>(&decode_kernel<EC_MODE, OUT_F32, SW, GV, NW>),
         hipFuncAttributeMaxDynamicSharedMemorySize, DEC_LDS_MAX);
@@ -986,21 +984,41 @@ hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
 }
 
 // SW = super-steps a stream wave takes: the workgroup's range split over its
-// waves (at most DEC_WAVES * DEC_SW_MAX super-steps, so SW <= DEC_SW_MAX).
-template <int EC_MODE, int OUT_F32, int GV>
+// NW waves (at most DEC_WAVES * DEC_SW_MAX super-steps, so SW <= DEC_SW_MAX).
+template <int EC_MODE, int OUT_F32, int GV, int NW>
 hipError_t launch_decode_sw(const LinearArgs &a, hipStream_t s)
 {
-    constexpr int NW = EC_MODE == 1 ? DEC_WAVES : DEC_WAVES_PLAIN;
     switch ((a.spw + NW - 1) / NW) {
-    case 1: return launch_decode_k<EC_MODE, OUT_F32, 1, GV>(a, s);
-    case 2: return launch_decode_k<EC_MODE, OUT_F32, 2, GV>(a, s);
-    case 3: return launch_decode_k<EC_MODE, OUT_F32, 3, GV>(a, s);
-    case 4: return launch_decode_k<EC_MODE, OUT_F32, 4, GV>(a, s);
-    case 5: return launch_decode_k<EC_MODE, OUT_F32, 5, GV>(a, s);
-    case 6: return launch_decode_k<EC_MODE, OUT_F32, 6, GV>(a, s);
-    case 7: return launch_decode_k<EC_MODE, OUT_F32, 7, GV>(a, s);
-    default: return launch_decode_k<EC_MODE, OUT_F32, 8, GV>(a, s);
+    case 1: return launch_decode_k<EC_MODE, OUT_F32, 1, GV, NW>(a, s);
+    case 2: return launch_decode_k<EC_MODE, OUT_F32, 2, GV, NW>(a, s);
+    case 3: return launch_decode_k<EC_MODE, OUT_F32, 3, GV, NW>(a, s);
+    case 4: return launch_decode_k<EC_MODE, OUT_F32, 4, GV, NW>(a, s);
+    case 5: return launch_decode_k<EC_MODE, OUT_F32, 5, GV, NW>(a, s);
+    case 6: return launch_decode_k<EC_MODE, OUT_F32, 6, GV, NW>(a, s);
+    case 7: return launch_decode_k<EC_MODE, OUT_F32, 7, GV, NW>(a, s);
+    default: return launch_decode_k<EC_MODE, OUT_F32, 8, GV, NW>(a, s);
     }
+}
+
+// Stream waves of a workgroup without the fused EC.  Eight waves halve each
+// wave's chain of super-steps, which pays only where a workgroup streams a long
+// K range (at least 32 super-steps) and the grid is at most one workgroup a CU;
+// otherwise four.  Measured on plain decode, 4 against 8 waves: 4096 x 4096
+// at 1 / 4 / 8 tokens 5.75 / 6.84 / 7.81 against 5.64 / 6.08 / 6.31 us, and
+// N = 2048, K = 8192 at 8 tokens 8.80 against 7.52 us; but K = 2048 at 16
+// tokens 5.13 against 6.66 us and N = 14336, K = 4096 at 8 tokens 15.4
+// against 18.2 us.
+int plain_waves(const LinearArgs &a)
+{
+    return (a.spw >= 32 && a.ncg * a.ksplit <= DEC_CUS) ? DEC_WAVES_PLAIN : DEC_WAVES;
+}
+
+template <int EC_MODE, int OUT_F32, int GV>
+hipError_t launch_decode_nw(const LinearArgs &a, hipStream_t s)
+{
+    if (EC_MODE != 1 && plain_waves(a) == DEC_WAVES_PLAIN)
+        return launch_decode_sw<EC_MODE, OUT_F32, GV, (EC_MODE != 1 ? DEC_WAVES_PLAIN : DEC_WAVES)>(a, s);
+    return launch_decode_sw<EC_MODE, OUT_F32, GV, DEC_WAVES>(a, s);
 }
 
 // One token takes the GEMV form (vector ALU); 2..16 tokens share every
@@ -1010,8 +1028,8 @@ template <int EC_MODE, int OUT_F32>
 hipError_t launch_decode_gv(const LinearArgs &a, hipStream_t s)
 {
     if (EC_MODE != 2 && a.M == 1)
-        return launch_decode_sw<EC_MODE, OUT_F32, (EC_MODE != 2 ? 1 : 0)>(a, s);
-    return launch_decode_sw<EC_MODE, OUT_F32, 0>(a, s);
+        return launch_decode_nw<EC_MODE, OUT_F32, (EC_MODE != 2 ? 1 : 0)>(a, s);
+    return launch_decode_nw<EC_MODE, OUT_F32, 0>(a, s);
 }
 
 template <int EC_MODE>

@@ -76,8 +76,9 @@ def errors(y, ref):
 
 
 # Two GPU kernels that add the same fp32 products in a different order (the
-# fused decode's 4 stream waves against the plain decode's 8) differ by a few
-# fp32 roundings of the partial sums: far below the parity bound.
+# fused decode's 4 stream waves against the 8 of a plain decode over a long K
+# range) differ by a few fp32 roundings of the partial sums: far below the
+# parity bound.
 RTOL_REORDER = 1e-5
 
 
