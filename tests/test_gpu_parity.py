@@ -199,6 +199,9 @@ RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 25
           # rank 32 with at least 128 token groups: 64-token pre-pass blocks over
           # K slices, a partial last block and a ragged last slice
           (2100, 96, 1056, 24),
+          # 64-token pre-pass blocks whose last block holds one partial group of
+          # 16 (the other three lie past M), K split into 4 slices of 520
+          (4100, 64, 2080, 32),
           # decode with K split over workgroups (16 tokens do not fit one
           # workgroup's LDS at this depth): three ranges, a ragged last one
           (12, 1000, 5024, 40)]
