@@ -390,7 +390,8 @@ def test_prepass_wait_timeout_gives_nan(r):
 @pytest.mark.parametrize("M", [1, 16, 128, 2048])
 def test_c5_stack_layers_sampled(M):
     ec_layer = gen.c5_ec_layers()[0]
-    for (layer, lin) in [(ec_layer, "down"), (ec_layer, "q"), (0 if ec_layer else 1, "up")]:
+    for (layer, lin) in [(ec_layer, "down"), (ec_layer, "q"), (ec_layer, "up"),
+                         (0 if ec_layer else 1, "up")]:
         d = gen.make_c5(layer, lin, M)
         rng = np.random.default_rng(M + layer)
         S = 1500
