@@ -18,7 +18,9 @@ The same line also carries:
     launch time of the fused and the plain decode kernel (one graph per M);
   * `roofline` of the fused decode kernel against 8 TB/s, plus the rate of a
     plain streaming read of the same 64 rotating weight buffers (the same-size
-    read floor, `stream_floor_GBps`);
+    read floor, `stream_floor_GBps`) and of one 1 GiB buffer
+    (`stream_floor_1GiB_GBps`), and the rate on the packed weights plus the EC
+    factors alone (`achieved_weights_ec_GBps`, the spec's headline count);
   * `prefill`: workload C4 (M = N = K = 4096, Student-t activations, EC rank 32
     soft gate): TFLOP/s with and without the EC, the EC overhead, the plain
     GEMM's fraction of the 2.5 PFLOP/s bf16 peak, and the CPU oracle on a
@@ -238,6 +240,16 @@ def stream_floor(torch, sp, bufs, steps, replays):
     return nbytes / (t["median"] * 1e-3) / 1e9, t["median"] * 1e3, nbytes
 
 
+def stream_floor_large(torch, sp, nbytes=1 << 30, replays=5):
+    """The same read over one 1 GiB buffer: the rate a long stream reaches."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    t = time_graph(torch, lambda n: [sp.spear_stream_read(buf, sink) for _ in range(n)], 1, replays)
+    del buf
+    return nbytes / (t["median"] * 1e-3) / 1e9
+
+
 def run_c2(args, torch, sp, gen):
     Ms = (1, 4, 8)
     d0 = gen.make(2, M=1)
@@ -274,6 +286,7 @@ def run_c2(args, torch, sp, gen):
     assert sp.spear_workspace_timeouts(wsp) == 0
     floor_gbs, floor_us, floor_bytes = stream_floor(torch, sp, [w.packed for w in ws],
                                                     args.steps, args.replays)
+    floor_large = stream_floor_large(torch, sp)
 
     per_step_bytes = 0.0
     per_step_plain = 0.0
@@ -284,6 +297,8 @@ def run_c2(args, torch, sp, gen):
     ms_step = t_ec["median"]
     launches = len(Ms)
     achieved = (per_step_bytes / launches) / (ms_step / launches * 1e-3) / 1e9
+    w_b, ec_b, _ = layer_bytes(1, N, K, r, True)            # packed weights plus EC factors
+    achieved_w_ec = (w_b + ec_b) / (ms_step / launches * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": round(per_step_bytes / (ms_step * 1e-3) / 1e9, 2),
@@ -320,6 +335,9 @@ def run_c2(args, torch, sp, gen):
                      "stream_floor_us_per_buffer": round(floor_us, 3),
                      "stream_floor_buffer_bytes": floor_bytes,
                      "frac_of_stream_floor": round(achieved / floor_gbs, 4),
+                     "stream_floor_1GiB_GBps": round(floor_large, 2),
+                     "achieved_weights_ec_GBps": round(achieved_w_ec, 2),
+                     "weights_ec_bytes_per_launch": round(w_b + ec_b),
                      "plain_frac_of_stream_floor": round(
                          (per_step_plain / launches) / (t_plain["median"] / launches * 1e-3)
                          / 1e9 / floor_gbs, 4)},
