@@ -407,6 +407,23 @@ def test_c5_stack_layers_sampled(M):
             assert np.array_equal(host(e.idx_out)[:n], gref["idx"])
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 4096, 4096), (4, 4112, 4096), (1, 2048, 8192), (8, 2048, 8192),
+                                   (12, 2048, 8192), (16, 1000, 4096)])
+def test_decode_stream_waves_parity(M, N, K):
+    """Plain and two-pass decode stream with 8 waves a workgroup where the
+    workgroup's K range is at least 32 super-steps and the grid at most 256
+    workgroups, else 4 (4112 channels: 257 groups; 12 and 16 tokens: K split):
+    both sides of that choice match the oracle, plain and with the EC."""
+    d = random_case(M, N, K, 32, oracle.CODES_U4, 0, seed=40 + M + N + K)
+    w = gpu_weights(d)
+    plain, _ = run_gpu(d, path=sp.PATH_DECODE, w=w, ec=False)
+    assert_close(plain, run_oracle(d, ec=None), f"plain decode {M}x{N}x{K}")
+    ref = run_oracle(d)
+    for path in (sp.PATH_DECODE, sp.PATH_DECODE_2PASS):
+        y, _ = run_gpu(d, path=path, w=w)
+        assert_close(y, ref, f"decode {M}x{N}x{K} path={path}")
+
+
 @pytest.mark.parametrize("K", [1056, 4096, 8192])
 @pytest.mark.parametrize("bias", [-4.0, 0.0, 4.0])
 def test_decode_one_token_hard_gate(K, bias):
