@@ -245,7 +245,11 @@ def stream_floor_large(torch, sp, nbytes=1 << 30, replays=5):
     buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     buf.fill_(1)
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
-    t = time_graph(torch, lambda n: [sp.spear_stream_read(buf, sink) for _ in range(n)], 1, replays)
+
+    def record(n):
+        for _ in range(n):
+            sp.spear_stream_read(buf, sink)
+    t = time_graph(torch, record, 1, replays)
     del buf
     return nbytes / (t["median"] * 1e-3) / 1e9
 
