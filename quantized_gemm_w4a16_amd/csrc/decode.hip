@@ -47,6 +47,8 @@
 //    whatever its grid (see epoch_claim), and every block of the launch reads
 //    the same upper half.  Graph replays and calls of other shapes on the same
 //    workspace therefore never see a stale tag as current.
+#include <atomic>
+
 #include "spear_internal.hpp"
 
 namespace spear {
@@ -60,6 +62,7 @@ namespace {
 // workgroup that holds nine token rows (2 x 79.3 KiB of LDS).
 constexpr int DEC_WAVES_PLAIN = 8;
 constexpr int64_t DEC_CUS = 256;                            // compute units of the chip
+constexpr int DEC_DEVICES = 64;                             // devices a process may use, at most
 
 template <int NW>
 struct DecShared {
@@ -963,15 +966,25 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
     }
 }
 
-// Dynamic LDS beyond 64 KiB must be enabled per kernel once.
+// Dynamic LDS beyond 64 KiB must be enabled per kernel, once on each device.
 template <int EC_MODE, int OUT_F32, int SW, int GV, int NW>
 hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
 {
-    static const hipError_t e = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&decode_kernel<EC_MODE, OUT_F32, SW, GV, NW>),
-        hipFuncAttributeMaxDynamicSharedMemorySize, DEC_LDS_MAX);
+    static std::atomic<int> enabled[DEC_DEVICES];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess)
         return e;
+    if (dev < 0 || dev >= DEC_DEVICES)
+        return hipErrorInvalidDevice;
+    if (!enabled[dev].load(std::memory_order_acquire)) {
+        e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&decode_kernel<EC_MODE, OUT_F32, SW, GV, NW>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, DEC_LDS_MAX);
+        if (e != hipSuccess)
+            return e;
+        enabled[dev].store(1, std::memory_order_release);
+    }
     const int64_t npwg = EC_MODE == 1 ? a.nprod : 0;
     const dim3 grid((unsigned)(npwg + a.ncg * a.ksplit));
     const dim3 block(64 * NW);
