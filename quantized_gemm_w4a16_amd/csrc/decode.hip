@@ -10,15 +10,17 @@
 //
 // Work decomposition (one launch):
 //  * a workgroup owns 16 output channels and a K range (all of K unless the
-//    activations of the range would not fit in LDS).  Each of its 4 stream
-//    waves owns a run of 128-deep super-steps: it DMAs the activations of
-//    exactly those steps into LDS (global_load_lds), issues every 16-byte load
-//    of its packed-weight share (HBM -> registers), and contracts each step as
-//    its load lands -- no workgroup barrier before the contraction.  Several
-//    tokens: bf16 MFMA with the tokens (padded to 16) on the MFMA's N side and
-//    a second MFMA against a constant-one operand for the per-token activation
-//    sums that remove the unpack offset.  One token: a wavefront-reduction
-//    GEMV (bf16 dot2 into fp32, four accumulators) and a VALU activation sum.
+//    activations of the range would not fit in LDS).  Each of its stream waves
+//    (4 with the fused EC; without it 8 over long K ranges on at most one
+//    workgroup a CU, else 4) owns a run of 128-deep super-steps: it DMAs the
+//    activations of exactly those steps into LDS (global_load_lds), issues
+//    every 16-byte load of its packed-weight share (HBM -> registers), and
+//    contracts each step as its load lands -- no workgroup barrier before the
+//    contraction.  Several tokens: bf16 MFMA with the tokens (padded to 16) on
+//    the MFMA's N side and a second MFMA against a constant-one operand for
+//    the per-token activation sums that remove the unpack offset.  One token:
+//    a wavefront-reduction GEMV (bf16 dot2 into fp32, four accumulators) and a
+//    VALU activation sum.
 //    The packed word order makes the unpacked pairs line up with the
 //    activations' own pairs, so the activations are used as loaded.
 //  * When K is split over workgroups, every range but the last stores its
@@ -27,8 +29,9 @@
 //  * EC (fused mode): the lowest block indices, which the dispatcher places
 //    first, are `nprod` producer workgroups.  Each reads about 8 KB of A per
 //    pair of tokens, at most 16 KB above 8 tokens (so a producer's share of
-//    the memory system is no larger than a stream workgroup's), computes the gate-logit partial (fp64) and A.x (MFMA; dot2 for one
-//    token) of every token over its K slice, reduces its 4 waves in LDS and
+//    the memory system is no larger than a stream workgroup's), computes the
+//    gate-logit partial (fp64) and A.x (MFMA; dot2 for one token) of every
+//    token over its K slice, reduces its 4 waves in LDS and
 //    stores the partials as 64-bit words {value, launch epoch}, one relaxed
 //    device-coherent store each, then leaves.  The epilogue of each channel
 //    group loads the words of its tokens (relaxed device-coherent loads, the 4
