@@ -797,15 +797,17 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     u32x4 pvh[G2_FM], pvl[G2_FM], pbf[G2_FN];
     if (ECPRE && wk == 0 && ks < a.rpad / 32)
         ec_load((int)ks, pvh, pvl, pbf);
-    // EC == 2, 64 x 64 tiles: the B rows of the slice's first rank chunk now
-    // (v comes from this launch's pre-pass blocks, at the end).
+    // EC == 2, 64 x 64 tiles: the B rows of the slice's first two rank chunks
+    // now (v comes from this launch's pre-pass blocks, at the end).
     constexpr bool PBF = G2_BN == 64;                     // registers to spare
+    u32x4 pbf2[G2_FN];
     if (EC == 2 && PBF && ks < a.rpad / 32) {
-        const int j = 32 * (int)ks + 8 * lg;
+        const int j = 32 * (int)ks + 8 * lg, j2 = j + 32 * (int)KS;
 #pragma unroll
         for (int fn = 0; fn < G2_FN; fn++) {
             const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
             pbf[fn] = (nn < N && j < a.r) ? ld16(a.B + nn * a.r + j) : zero4();
+            pbf2[fn] = (nn < N && j2 < a.r) ? ld16(a.B + nn * a.r + j2) : zero4();
         }
     }
     // The epilogue's scales and zero-point bytes, loaded now so that their round
@@ -1046,43 +1048,55 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     }
     if (EC == 2 && ks < a.rpad / 32) {
         // v of the tile's tokens as tagged words from the launch's pre-pass
-        // blocks: word {hi | lo << 16, epoch} per (token, rank).  Each thread
-        // loads its share of the tile's words into LDS (stage buffer 0, free
-        // after the main loop) until every tag is this launch's; when they are
-        // not all there at the first try, a wave polls one word (one request)
-        // before it reloads, so that early tiles do not flood the memory system
-        // the pre-pass needs.  Bounded; an expired wait makes the whole tile
-        // NaN (its EC term is unknown) and is counted.
+        // blocks: word {hi | lo << 16, epoch} per (token, rank).  The slice's rank
+        // chunks are taken two at a time: each thread loads its share of both
+        // chunks' words into LDS (stage buffer 0, free after the main loop) in
+        // one poll, until every tag is this launch's, so a rank above 32 costs
+        // no second round trip; when they are not all there at the first try,
+        // a wave polls one word (one request) before it reloads, so that early
+        // tiles do not flood the memory system the pre-pass needs.  Bounded; an
+        // expired wait makes the whole tile NaN (its EC term is unknown) and is
+        // counted.
         const uint64_t *vtag = reinterpret_cast<const uint64_t *>(a.ws + a.L.vtag);
         const uint32_t tag = s_tagg;
         const int rpad = a.rpad, r = a.r;
-        uint32_t *s_v = reinterpret_cast<uint32_t *>(s_x0);          // [G2_BM][32] payloads
-        static_assert(G2_BM * 32 * 4 <= G2_XB && (G2_BM * 32) % G2_NT == 0, "v staging");
-        constexpr int VW = G2_BM * 32 / G2_NT;                        // words a thread loads
-        for (int64_t t = ks; t < rpad / 32; t += KS) {
-            const int j = 32 * (int)t + 8 * lg;
-            u32x4 bf[G2_FN];
+        const int64_t nch = rpad / 32;
+        uint32_t *s_v = reinterpret_cast<uint32_t *>(s_x0);          // [2][G2_BM][32] payloads
+        static_assert(2 * G2_BM * 32 * 4 <= G2_XB && (G2_BM * 32) % G2_NT == 0, "v staging");
+        constexpr int VW = G2_BM * 32 / G2_NT;                        // words a thread loads a chunk
+        for (int64_t t = ks; t < nch; t += 2 * KS) {
+            const bool two = t + KS < nch;                            // uniform
+            u32x4 bf[2][G2_FN];
 #pragma unroll
-            for (int fn = 0; fn < G2_FN; fn++) {
-                const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
-                bf[fn] = (PBF && t == ks) ? pbf[fn]
-                         : (nn < N && j < r) ? ld16(a.B + nn * r + j) : zero4();
+            for (int h = 0; h < 2; h++) {
+                const int j = 32 * (int)(t + h * KS) + 8 * lg;
+#pragma unroll
+                for (int fn = 0; fn < G2_FN; fn++) {
+                    const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
+                    bf[h][fn] = (PBF && t == ks) ? (h == 0 ? pbf[fn] : pbf2[fn])
+                                : (nn < N && j < r && (h == 0 || two)) ? ld16(a.B + nn * r + j) : zero4();
+                }
             }
             bool ok = true;
             for (uint32_t it = 0;; it++) {
                 bool good = true;
-                uint64_t w[VW];
+                uint64_t w[2][VW];
 #pragma unroll
-                for (int q = 0; q < VW; q++) {
-                    const int e = tid + G2_NT * q;                      // token e / 32, rank e % 32
-                    const int64_t mm = m0 + e / 32 < M ? m0 + e / 32 : M - 1;
-                    w[q] = load_tagged(vtag + mm * rpad + 32 * t + e % 32);
-                }
+                for (int h = 0; h < 2; h++)
 #pragma unroll
-                for (int q = 0; q < VW; q++) {
-                    good &= (uint32_t)(w[q] >> 32) == tag;
-                    s_v[tid + G2_NT * q] = (uint32_t)w[q];
-                }
+                    for (int q = 0; q < VW; q++) {
+                        const int e = tid + G2_NT * q;                  // token e / 32, rank e % 32
+                        const int64_t mm = m0 + e / 32 < M ? m0 + e / 32 : M - 1;
+                        w[h][q] = (h == 0 || two) ? load_tagged(vtag + mm * rpad + 32 * (t + h * KS) + e % 32)
+                                                  : (uint64_t)tag << 32;
+                    }
+#pragma unroll
+                for (int h = 0; h < 2; h++)
+#pragma unroll
+                    for (int q = 0; q < VW; q++) {
+                        good &= (uint32_t)(w[h][q] >> 32) == tag;
+                        s_v[h * G2_BM * 32 + tid + G2_NT * q] = (uint32_t)w[h][q];
+                    }
                 if (__all(good))
                     break;
                 if (it >= a.wait_limit) {
@@ -1093,7 +1107,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                     // not there yet: poll one word (one request a wave) until the
                     // tile's last token has it, rather than reload them all
                     const int64_t ml = m0 + G2_BM - 1 < M ? m0 + G2_BM - 1 : M - 1;
-                    const uint64_t *probe = vtag + ml * rpad + 32 * t + 31;
+                    const uint64_t *probe = vtag + ml * rpad + 32 * (two ? t + KS : t) + 31;
                     for (uint32_t ip = 0; ip < a.wait_limit; ip++) {
                         if ((uint32_t)(load_tagged(probe) >> 32) == tag)
                             break;
@@ -1118,23 +1132,29 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                 continue;
             }
 #pragma unroll
-            for (int fm = 0; fm < G2_FM; fm++) {
-                const int row = (wm * G2_FM + fm) * 16 + lr;
-                const u32x4 p0 = *reinterpret_cast<const u32x4 *>(s_v + row * 32 + 8 * lg);
-                const u32x4 p1 = *reinterpret_cast<const u32x4 *>(s_v + row * 32 + 8 * lg + 4);
-                const uint32_t w8[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
-                const bool mv = m0 + row < M;
-                u32x4 vh, vl;
+            for (int h = 0; h < 2; h++) {
+                if (h == 1 && !two)
+                    break;
 #pragma unroll
-                for (int p = 0; p < 4; p++) {
-                    const uint32_t w0 = w8[2 * p], w1 = w8[2 * p + 1];
-                    vh[p] = mv ? (w0 & 0xFFFFu) | (w1 << 16) : 0u;
-                    vl[p] = mv ? (w0 >> 16) | (w1 & 0xFFFF0000u) : 0u;
-                }
+                for (int fm = 0; fm < G2_FM; fm++) {
+                    const int row = (wm * G2_FM + fm) * 16 + lr;
+                    const uint32_t *sv = s_v + h * G2_BM * 32 + row * 32 + 8 * lg;
+                    const u32x4 p0 = *reinterpret_cast<const u32x4 *>(sv);
+                    const u32x4 p1 = *reinterpret_cast<const u32x4 *>(sv + 4);
+                    const uint32_t w8[8] = {p0[0], p0[1], p0[2], p0[3], p1[0], p1[1], p1[2], p1[3]};
+                    const bool mv = m0 + row < M;
+                    u32x4 vh, vl;
 #pragma unroll
-                for (int fn = 0; fn < G2_FN; fn++) {
-                    acc[fn][fm] = mfma16(bf[fn], vh, acc[fn][fm]);
-                    acc[fn][fm] = mfma16(bf[fn], vl, acc[fn][fm]);
+                    for (int p = 0; p < 4; p++) {
+                        const uint32_t w0 = w8[2 * p], w1 = w8[2 * p + 1];
+                        vh[p] = mv ? (w0 & 0xFFFFu) | (w1 << 16) : 0u;
+                        vl[p] = mv ? (w0 >> 16) | (w1 & 0xFFFF0000u) : 0u;
+                    }
+#pragma unroll
+                    for (int fn = 0; fn < G2_FN; fn++) {
+                        acc[fn][fm] = mfma16(bf[h][fn], vh, acc[fn][fm]);
+                        acc[fn][fm] = mfma16(bf[h][fn], vl, acc[fn][fm]);
+                    }
                 }
             }
             __syncthreads();                                          // s_v is rewritten next
