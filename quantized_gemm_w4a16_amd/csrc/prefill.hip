@@ -798,10 +798,11 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     if (ECPRE && wk == 0 && ks < a.rpad / 32)
         ec_load((int)ks, pvh, pvl, pbf);
     // EC == 2, 64 x 64 tiles: the B rows of the slice's first two rank chunks
-    // now (v comes from this launch's pre-pass blocks, at the end).
+    // now (v comes from this launch's pre-pass blocks, at the end), in the
+    // waves that apply the EC term (the first of each depth pair).
     constexpr bool PBF = G2_BN == 64;                     // registers to spare
     u32x4 pbf2[G2_FN];
-    if (EC == 2 && PBF && ks < a.rpad / 32) {
+    if (EC == 2 && PBF && wk == 0 && ks < a.rpad / 32) {
         const int j = 32 * (int)ks + 8 * lg, j2 = j + 32 * (int)KS;
 #pragma unroll
         for (int fn = 0; fn < G2_FN; fn++) {
@@ -1064,6 +1065,10 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
         uint32_t *s_v = reinterpret_cast<uint32_t *>(s_x0);          // [2][G2_BM][32] payloads
         static_assert(2 * G2_BM * 32 * 4 <= G2_XB && (G2_BM * 32) % G2_NT == 0, "v staging");
         constexpr int VW = G2_BM * 32 / G2_NT;                        // words a thread loads a chunk
+        // With the depth split only the first wave of each pair applies the
+        // term (the second's sums are in it already); both load words and take
+        // the barriers.
+        const bool apply = G2_WK == 1 || wk == 0;                     // uniform
         for (int64_t t = ks; t < nch; t += 2 * KS) {
             const bool two = t + KS < nch;                            // uniform
             u32x4 bf[2][G2_FN];
@@ -1074,7 +1079,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                 for (int fn = 0; fn < G2_FN; fn++) {
                     const int64_t nn = n0 + (wn * G2_FN + fn) * 16 + lr;
                     bf[h][fn] = (PBF && t == ks) ? (h == 0 ? pbf[fn] : pbf2[fn])
-                                : (nn < N && j < r && (h == 0 || two)) ? ld16(a.B + nn * r + j) : zero4();
+                                : (apply && nn < N && j < r && (h == 0 || two)) ? ld16(a.B + nn * r + j)
+                                                                                : zero4();
                 }
             }
             bool ok = true;
@@ -1133,7 +1139,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
             }
 #pragma unroll
             for (int h = 0; h < 2; h++) {
-                if (h == 1 && !two)
+                if ((h == 1 && !two) || !apply)
                     break;
 #pragma unroll
                 for (int fm = 0; fm < G2_FM; fm++) {
@@ -1157,7 +1163,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
                     }
                 }
             }
-            __syncthreads();                                          // s_v is rewritten next
+            if (t + 2 * KS < nch)
+                __syncthreads();                                      // s_v is rewritten next
         }
     }
     if (EC == 1 && ks < a.rpad / 32) {
