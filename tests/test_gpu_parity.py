@@ -196,6 +196,9 @@ RAGGED = [(1, 16, 32, 8), (3, 40, 96, 16), (16, 1000, 160, 40), (5, 17, 1056, 25
           # K split over workgroups with a K tail and EC rank chunks spread over
           # the slices; 64 x 64 tiles up to 128 tokens, 128 x 256 above
           (64, 260, 1184, 96), (65, 700, 1280, 48), (128, 2050, 1024, 32), (129, 300, 1024, 16),
+          # 128 x 256 tiles over two K slices with the pre-pass in the GEMM's
+          # launch: each slice's epilogue takes two rank chunks in one poll
+          (160, 300, 1024, 128),
           # rank 32 with at least 128 token groups: 64-token pre-pass blocks over
           # K slices, a partial last block and a ragged last slice
           (2100, 96, 1056, 24),
