@@ -254,6 +254,20 @@ def stream_floor_large(torch, sp, nbytes=1 << 30, replays=5):
     return nbytes / (t["median"] * 1e-3) / 1e9
 
 
+def launch_floor(torch, sp, replays, launches=200):
+    """Fixed cost of one dependent launch in a captured graph: back-to-back
+    launches of the library's read kernel over 16 KiB (one workgroup), in
+    microseconds a launch."""
+    buf = torch.ones(16384, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def record(n):
+        for _ in range(n):
+            sp.spear_stream_read(buf, sink)
+    t = time_graph(torch, record, launches, replays)
+    return t["median"] * 1e3
+
+
 def run_c2(args, torch, sp, gen):
     Ms = (1, 4, 8)
     d0 = gen.make(2, M=1)
@@ -574,6 +588,7 @@ def run_c5(args, torch, sp, gen):
     t_ec = time_graph(torch, steps_fn(True), args.steps, args.replays)["median"] * args.steps
     t_plain = time_graph(torch, steps_fn(False), args.steps, args.replays)["median"] * args.steps
     assert sp.spear_workspace_timeouts(wsp) == 0
+    floor_us = launch_floor(torch, sp, args.replays)
     byts = sum(sum(layer_bytes(M, N, K, r, True)) for (N, K, w, ec, r) in layers)
     flops = sum(2.0 * M * N * K + (2.0 * M * K * r + 2.0 * M * r * N if r else 0.0)
                 for (N, K, w, ec, r) in layers)
@@ -596,6 +611,12 @@ def run_c5(args, torch, sp, gen):
         "plain_stack_ms": round(t_plain / args.steps, 4),
         "ec_share": round((t_ec - t_plain) / t_ec, 4),
         "ec_overhead": round(t_ec / t_plain - 1.0, 4),
+        "launch_floor": {"us_per_launch": round(floor_us, 3), "launches_per_step": len(layers),
+                         "ms_per_step": round(floor_us * len(layers) / 1e3, 4),
+                         "share_of_stack": round(floor_us * len(layers) / 1e3 / ms, 4),
+                         "what": "graph-captured back-to-back launches of the library's read kernel "
+                                 "over 16 KiB (one workgroup): the fixed cost each of the stack's "
+                                 "dependent launches pays"},
         "roofline": {"bound": "mfma" if big else "hbm", "achieved": round(val, 2), "peak": peak,
                      "unit": unit, "frac": round(val / peak, 4), "traffic": None,
                      "kernel": "whole stack (all kernels)"},
