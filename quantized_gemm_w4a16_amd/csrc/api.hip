@@ -24,14 +24,25 @@ static inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 // more each; fewer producers keep the partials every epilogue loads
 // (producers x tokens x ranks) small.  Above 8 tokens the producers' own loads
 // are the longest path, so each reads at most 2 PROD_BYTES of A, as long as
-// the partials an epilogue loads stay within PROD_WORDS words.
-static int64_t ec_producers(int64_t mr, int64_t K, int64_t rpad, int64_t *prod_k)
+// the partials an epilogue loads stay within PROD_WORDS words.  A layer with
+// more channel groups than CUs (two stream workgroups a CU) takes producers
+// that read a quarter as much each, and above 8 tokens twice the words: there
+// the producers' loads are the longer path at 4 to 16 tokens (N = 8192,
+// K = 2048: 13.2 / 14.2 / 14.6 -> 10.9 / 11.9 / 13.2 us at 4 / 8 / 16 tokens),
+// while the same change slows layers of up to one group a CU (C2: 1020 ->
+// 921 GB/s).
+constexpr int64_t EC_WIDE_GROUPS = 256;                     // channel groups: one a CU of the chip
+
+static int64_t ec_producers(int64_t mr, int64_t K, int64_t rpad, int64_t ncg, int64_t *prod_k)
 {
+    const bool wide = ncg > EC_WIDE_GROUPS;
+    const int64_t pbytes = wide ? PROD_BYTES / 4 : PROD_BYTES;
+    const int64_t pwords = wide ? 2 * PROD_WORDS : PROD_WORDS;
     const int64_t per = mr > 8 ? 2 : cdiv(mr, 2);
-    int64_t nprod = cdiv(K * rpad * 2, PROD_BYTES * per);
+    int64_t nprod = cdiv(K * rpad * 2, pbytes * per);
     if (mr > 8) {
-        const int64_t cap = PROD_WORDS / (mr * rpad);
-        const int64_t base = cdiv(K * rpad * 2, PROD_BYTES * cdiv(mr, 2));
+        const int64_t cap = pwords / (mr * rpad);
+        const int64_t base = cdiv(K * rpad * 2, pbytes * cdiv(mr, 2));
         const int64_t lim = cap > base ? cap : base;       // never fewer than before
         nprod = nprod > lim ? lim : nprod;
     }
@@ -106,12 +117,12 @@ WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r)
     L.spw = cdiv(S, L.ksplit);
     L.rpad = r > 0 ? cdiv(r, 32) * 32 : 0;
     L.mpad = cdiv(M > 0 ? M : 1, 16) * 16;
-    L.nprod = r > 0 ? ec_producers(mr, K, L.rpad, &L.prod_k) : 0;
+    L.nprod = r > 0 ? ec_producers(mr, K, L.rpad, L.ncg, &L.prod_k) : 0;
     // The partials region is sized for the most producers any token count
     // uses (one token), so that a workspace sized for some M also serves every
     // smaller M, and the decode path after the prefill path.
     int64_t pk1 = 0;
-    const int64_t nprod_max = r > 0 ? ec_producers(1, K, L.rpad, &pk1) : 0;
+    const int64_t nprod_max = r > 0 ? ec_producers(1, K, L.rpad, L.ncg, &pk1) : 0;
 
     size_t off = 0;
     L.hdr = off;
