@@ -390,6 +390,9 @@ static spear_status validate_linear(const spear_bf16 *x, int64_t M, const spear_
         return SPEAR_E_WORKSPACE;
     if (L.ncg * L.ksplit > GRID_MAX || cdiv(N, 64) * cdiv(M, 64) > GRID_MAX)
         return SPEAR_E_SHAPE;
+    // the decode kernels take their workspace offsets as 32-bit values
+    if ((path == SPEAR_PATH_DECODE || path == SPEAR_PATH_DECODE_2PASS) && L.active > 0xFFFFFFFFull)
+        return SPEAR_E_SHAPE;
     *path_io = path;
     return SPEAR_OK;
 }
@@ -410,11 +413,11 @@ static void fill_args(LinearArgs &a, const spear_bf16 *x, int64_t M, const spear
     a.M = M;
     a.N = N;
     a.K = K;
-    a.ncg = L.ncg;
-    a.ksplit = L.ksplit;
-    a.spw = L.spw;
-    a.nprod = L.nprod;
-    a.prod_k = L.prod_k;
+    a.ncg = (int32_t)L.ncg;
+    a.ksplit = (int32_t)L.ksplit;
+    a.spw = (int32_t)L.spw;
+    a.nprod = (int32_t)L.nprod;
+    a.prod_k = (int32_t)L.prod_k;
     a.mpad = L.mpad;
     {
         // EC pre-pass: few token groups split K so that up to about 256
@@ -432,6 +435,16 @@ static void fill_args(LinearArgs &a, const spear_bf16 *x, int64_t M, const spear
     a.g_bn = gemm_bn(a.g_bm);
     a.g_ks = gemm_ks(M, N, K, path == SPEAR_PATH_PREFILL_LARGE);
     a.L = L;
+    // 32-bit copies for the decode kernels (checked on their paths; the
+    // others read only hdr and epoch from here, at the start of the layout)
+    a.D.hdr = (uint32_t)L.hdr;
+    a.D.epoch = (uint32_t)L.epoch;
+    a.D.splitp = (uint32_t)L.splitp;
+    a.D.pu = (uint32_t)L.pu;
+    a.D.pz = (uint32_t)L.pz;
+    a.D.vhi = (uint32_t)L.vhi;
+    a.D.vlo = (uint32_t)L.vlo;
+    a.D.active = (uint32_t)L.active;
     a.out_f32 = out_dtype == SPEAR_OUT_F32;
     const uint32_t wl = g_wait_limit.load(std::memory_order_relaxed);
     a.wait_limit = wl ? wl : DEFAULT_WAIT_LIMIT;

@@ -148,15 +148,15 @@ __device__ void ec_produce(const LinearArgs &a, int64_t p, int wave, int lane, u
     const int rpad = a.rpad, r = a.r;
     uint64_t claimed = opaque_zero64();
     if (tid == 0)
-        claimed = epoch_claim(a);                         // back long before it is used
+        claimed = epoch_claim(a, a.grid);                 // back long before it is used
 
     const int64_t k0 = (p * DEC_WAVES + wave) * a.prod_k;
     const int64_t k1 = (k0 + a.prod_k < K) ? k0 + a.prod_k : K;
     float *lu = reinterpret_cast<float *>(lds);
     double *lz = reinterpret_cast<double *>(lds + EC_LDS_U);
     uint32_t *ltag = reinterpret_cast<uint32_t *>(lds + EC_LDS_U + EC_LDS_Z);
-    uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.L.pu);
-    uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.L.pz);
+    uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.D.pu);
+    uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.D.pz);
 
     double zp = 0.0;
     for (int jp = 0; jp < rpad / 32; jp++) {
@@ -240,15 +240,15 @@ __device__ void ec_produce_gv(const LinearArgs &a, int64_t p, int wave, int lane
     const int rpad = a.rpad, r = a.r;
     uint64_t claimed = opaque_zero64();
     if (tid == 0)
-        claimed = epoch_claim(a);                         // back long before it is used
+        claimed = epoch_claim(a, a.grid);                 // back long before it is used
 
     const int64_t k0 = (p * DEC_WAVES + wave) * a.prod_k;
     const int64_t k1 = (k0 + a.prod_k < K) ? k0 + a.prod_k : K;   // k1 - k0: multiple of 32
     float *lu = reinterpret_cast<float *>(lds);                   // [wave][32]
     double *lz = reinterpret_cast<double *>(lds + EC_LDS_U);      // [wave]
     uint32_t *ltag = reinterpret_cast<uint32_t *>(lds + EC_LDS_U + EC_LDS_Z);
-    uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.L.pu);
-    uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.L.pz);
+    uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.D.pu);
+    uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.D.pz);
 
     double zp = 0.0;
     for (int jp = 0; jp < rpad / 32; jp++) {
@@ -330,8 +330,8 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
     const int64_t M = a.M, N = a.N, np = a.nprod;
     const int64_t n = cg * 16 + lr;
     const int rpad = a.rpad, r = a.r;
-    const uint64_t *pu = reinterpret_cast<const uint64_t *>(a.ws + a.L.pu);
-    const uint64_t *pz = reinterpret_cast<const uint64_t *>(a.ws + a.L.pz);
+    const uint64_t *pu = reinterpret_cast<const uint64_t *>(a.ws + a.D.pu);
+    const uint64_t *pz = reinterpret_cast<const uint64_t *>(a.ws + a.D.pz);
     float *lu = reinterpret_cast<float *>(lds);               // [wave][token][32]
     double *lz = reinterpret_cast<double *>(lds + EC_LDS_U);  // [wave][token]
     int32_t *lok = reinterpret_cast<int32_t *>(lds + EC_LDS_U + EC_LDS_Z);
@@ -392,7 +392,7 @@ __device__ f32x4 ec_consume(const LinearArgs &a, const u32x4 *bpre, int64_t cg, 
                 if (it >= a.wait_limit) {
                     ok = false;
                     if (lane == 0)
-                        atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+                        atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.D.hdr) + HDR_TIMEOUTS, 1u);
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
@@ -544,7 +544,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
     static_assert(EC_MODE != 1 || NW == DEC_WAVES, "the fused EC's exchange is laid out for 4 waves");
     __shared__ DecShared<NW> sh;
     extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];
-    pin_args(a);
+    pin_dec_args(a);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
 
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
     // needed in the epilogue.
     uint64_t claimed = opaque_zero64();
     if ((EC_MODE == 1 || a.ksplit > 1) && tid == 0)
-        claimed = epoch_claim(a);
+        claimed = epoch_claim(a, a.grid);
 
     // Wait for everything but the weight stream (the SW youngest loads) and for
     // the LDS zero fills: the wave's activations are then in LDS.  The weight
@@ -833,7 +833,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
         //    per workgroup would write back the whole L2 (measured: 20 against
         //    8.7 us for M = 16, K = 8192).
         if (ksplit > 1) {
-            uint64_t *sp = reinterpret_cast<uint64_t *>(a.ws + a.L.splitp);
+            uint64_t *sp = reinterpret_cast<uint64_t *>(a.ws + a.D.splitp);
             const uint32_t tag = sh.u32[0];
             epi = ks == ksplit - 1;
             if (wave == 0 && lr < M) {
@@ -871,7 +871,7 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
                             if (it >= a.wait_limit) {
                                 ok = false;
                                 if (lane == 0)
-                                    atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+                                    atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.D.hdr) + HDR_TIMEOUTS, 1u);
                                 break;
                             }
                             __builtin_amdgcn_s_sleep(1);
@@ -917,9 +917,9 @@ __global__ __launch_bounds__(64 * NW) void decode_kernel(const LinearArgs a)
                 yv[i] += ec_e[i];
         } else if (EC_MODE == 2) {
             // v precomputed by the pre-pass (bf16 hi + lo, zero for skipped tokens)
-            const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
-            const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
-            const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
+            const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.D.active);
+            const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.D.vhi);
+            const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.D.vlo);
             const int act = (lr < M) ? active[lr] : 0;
             if (__ballot(act) != 0ull) {
                 f32x4 e = {0.f, 0.f, 0.f, 0.f};
@@ -989,13 +989,15 @@ hipError_t launch_decode_k(const LinearArgs &a, hipStream_t s)
         enabled[dev].store(1, std::memory_order_release);
     }
     const int64_t npwg = EC_MODE == 1 ? a.nprod : 0;
-    const dim3 grid((unsigned)(npwg + a.ncg * a.ksplit));
+    const dim3 grid((unsigned)(npwg + (int64_t)a.ncg * a.ksplit));
     const dim3 block(64 * NW);
     size_t lds = (size_t)(a.M + 1) * (size_t)(a.spw * 256 + 16);
     const size_t ec_lds = EC_LDS + (a.gate_h > 0 ? EC_LDS_VG : 0);
     if (EC_MODE == 1 && lds < ec_lds)
         lds = ec_lds;                                     // EC partials meet in the same LDS
-    hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW, GV, NW>), grid, block, lds, s, a);
+    LinearArgs ka = a;
+    ka.grid = grid.x;                                     // the kernels read it instead of gridDim
+    hipLaunchKernelGGL((decode_kernel<EC_MODE, OUT_F32, SW, GV, NW>), grid, block, lds, s, ka);
     return hipGetLastError();
 }
 

@@ -390,7 +390,7 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
     pin_args(a);
     uint64_t claimed = opaque_zero64();
     if (a.pre_ks > 1 && threadIdx.x == 0)
-        claimed = epoch_claim(a);                         // back long before it is used
+        claimed = epoch_claim(a, gridDim.x);              // back long before it is used
     const PreShared<PRE_WAVES> sh = {s_u, s_u + PRE_WAVES / 2, s_z, s_wg, s_uw, s_zw, s_g, s_act,
                                      &s_tag, &s_bad, s_hid};
     prepass_body<PRE_WAVES>(a, blockIdx.x, sh, claimed, false);
@@ -440,7 +440,7 @@ __global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
     const int64_t M = a.M, K = a.K, KS = a.pre_ks, r = a.r;
     uint64_t claimed = opaque_zero64();
     if (KS > 1 && tid == 0)
-        claimed = epoch_claim(a);
+        claimed = epoch_claim(a, gridDim.x);
     const int64_t grp = blockIdx.x / KS, ks = blockIdx.x % KS;
     const int64_t m0 = grp * 16;
     const int64_t T = K / 32;
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     uint64_t claimed = opaque_zero64();
     if constexpr (EC == 2) {
         if (tid == 0)
-            claimed = epoch_claim(a);
+            claimed = epoch_claim(a, gridDim.x);
         if ((int64_t)blockIdx.x < a.npre) {
             // u: waves 0 .. PW/2 - 1 in s_x0, the others in s_x1; the workgroup's u in
             // s_x2; logit partials and w_g in c0 (s_w0, or s_x3 when the

@@ -143,7 +143,19 @@ struct WsLayout {
 WsLayout ws_layout(int64_t M, int64_t N, int64_t K, int32_t r);
 
 // ------------------------------------------------------------- kernel params
+// Offsets (bytes) of the workspace regions the decode kernels use.  A decode
+// call's layout holds only small regions ahead of them (the host checks that
+// they fit 32 bits).
+struct DecOffsets {
+    uint32_t hdr, epoch, splitp, pu, pz, vhi, vlo, active;
+};
+
 struct LinearArgs {
+    // The leading block (212 bytes, four 64-byte lines) is what the decode
+    // kernels load at entry.  Each further 64-byte line of arguments a kernel
+    // loads adds about 0.35 us to its launch (measured in graph replay: 3.1 us
+    // for one line, 3.9 us for four, 5.0 us for eight), so the fields they use
+    // come first and no wider than they need to be.
     const uint16_t *x;
     const uint8_t *packed;
     const float *scales;
@@ -154,24 +166,31 @@ struct LinearArgs {
     float *g_out;
     int32_t *idx_out;
     int32_t *nact_out;
+    int64_t M, N, K;
     double thr;      // logit(tau) for the hard gate
     float b;
     int32_t hard;
     int32_t r, rpad;
-    int64_t M, N, K;
-    int64_t ncg, ksplit, spw, nprod, prod_k, mpad;
+    int32_t ncg, ksplit, spw, nprod, prod_k;   // decode: channel groups, K ranges, EC producers
+    uint32_t wait_limit;
+    int32_t out_f32;
+    int32_t gate_h;  // vector gate: hidden width (0: scalar gate only)
+    float alpha;
+    DecOffsets D;
+    uint32_t grid;   // decode: the launch's workgroups (gridDim lives in a line of its own)
+    // The rest: the vector gate MLP, the prefill tiling and the full layout.
+    const float *gw1, *gc1, *gw2, *gc2;   // vector gate MLP (gate_h > 0)
+    int64_t mpad;
     int64_t pre_ks;  // EC pre-pass: K slices per token group
     int64_t g_bm;    // MFMA GEMM: tokens per tile (64 or 128)
     int64_t g_bn;    // MFMA GEMM: channels per tile (64 with 64-token tiles, else 256)
     int64_t g_ks;    // MFMA GEMM: K slices per tile (partials reduced by a second launch)
     int64_t npre;    // K-split GEMM with the EC pre-pass in its launch: leading pre-pass blocks
-    const float *gw1, *gc1, *gw2, *gc2;   // vector gate MLP (gate_h > 0)
-    int32_t gate_h;
-    float alpha;
     WsLayout L;
-    uint32_t wait_limit;
-    int32_t out_f32;
 };
+static_assert(offsetof(LinearArgs, gw1) == 216 && offsetof(LinearArgs, D) == 180 &&
+                  offsetof(LinearArgs, grid) == 212,
+              "the decode kernels' leading block");
 
 // Explicit counter waits (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
 // expcnt 6:4, lgkmcnt 11:8) and a barrier without the fence of
@@ -206,10 +225,24 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
     pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
     pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
     pin_arg(a.pre_ks); pin_arg(a.g_ks); pin_arg(a.g_bn); pin_arg(a.npre); pin_arg(a.L.vtag); pin_arg(a.L.gpart); pin_arg(a.L.preu); pin_arg(a.L.prez);
-    pin_arg(a.L.hdr); pin_arg(a.L.epoch); pin_arg(a.L.zeros); pin_arg(a.L.splitp); pin_arg(a.L.pu);
+    pin_arg(a.L.hdr); pin_arg(a.D.epoch); pin_arg(a.L.zeros); pin_arg(a.L.splitp); pin_arg(a.L.pu);
     pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active); pin_arg(a.L.idx);
     pin_arg(a.wait_limit); pin_arg(a.out_f32);
     pin_arg(a.gw1); pin_arg(a.gc1); pin_arg(a.gw2); pin_arg(a.gc2); pin_arg(a.gate_h); pin_arg(a.alpha);
+}
+
+// The decode kernels' arguments: the leading block only (the vector gate's
+// weights are loaded where that path needs them).
+__device__ __forceinline__ void pin_dec_args(const LinearArgs &a)
+{
+    pin_arg(a.x); pin_arg(a.packed); pin_arg(a.scales); pin_arg(a.zeros); pin_arg(a.A);
+    pin_arg(a.B); pin_arg(a.wg); pin_arg(a.y); pin_arg(a.ws); pin_arg(a.g_out);
+    pin_arg(a.idx_out); pin_arg(a.nact_out); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K);
+    pin_arg(a.thr); pin_arg(a.b); pin_arg(a.hard); pin_arg(a.r); pin_arg(a.rpad);
+    pin_arg(a.ncg); pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k);
+    pin_arg(a.wait_limit); pin_arg(a.out_f32); pin_arg(a.gate_h); pin_arg(a.alpha);
+    pin_arg(a.D.hdr); pin_arg(a.D.epoch); pin_arg(a.D.splitp); pin_arg(a.D.pu);
+    pin_arg(a.D.pz); pin_arg(a.D.vhi); pin_arg(a.D.vlo); pin_arg(a.D.active); pin_arg(a.grid);
 }
 
 // ---------------------------------------------- tagged cross-workgroup exchange
@@ -218,11 +251,11 @@ __device__ __forceinline__ void pin_args(const LinearArgs &a)
 // adds 2^32 - (n - 1), the n - 1 others of the class 1 each, and block 0 adds
 // 2^32 to the counters no block of a small grid uses.  Between launches all
 // counters hold the same multiple of 2^32, so every block of a launch reads the
-// same upper half whatever the order of the adds.
-__device__ __forceinline__ uint64_t epoch_claim(const LinearArgs &a)
+// same upper half whatever the order of the adds.  G is the launch's grid size.
+__device__ __forceinline__ uint64_t epoch_claim(const LinearArgs &a, uint32_t G)
 {
-    uint8_t *base = a.ws + a.L.epoch;
-    const uint32_t G = gridDim.x, bid = blockIdx.x, c = bid % EPOCH_CTRS;
+    uint8_t *base = a.ws + a.D.epoch;
+    const uint32_t bid = blockIdx.x, c = bid % EPOCH_CTRS;
     uint64_t add = 1;
     if (bid < EPOCH_CTRS)
         add = (1ull << 32) - ((G - 1 - c) / EPOCH_CTRS + 1) + 1;
