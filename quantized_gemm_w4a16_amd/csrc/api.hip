@@ -429,12 +429,22 @@ static void fill_args(LinearArgs &a, const spear_bf16 *x, int64_t M, const spear
             const int64_t most = T / 8 > 0 ? T / 8 : 1;
             ks = ks < most ? ks : most;
         }
-        a.pre_ks = ks;
+        a.pre_ks = (int32_t)ks;
     }
-    a.g_bm = gemm_bm(M, path == SPEAR_PATH_PREFILL_LARGE);
-    a.g_bn = gemm_bn(a.g_bm);
-    a.g_ks = gemm_ks(M, N, K, path == SPEAR_PATH_PREFILL_LARGE);
+    a.g_bm = (int32_t)gemm_bm(M, path == SPEAR_PATH_PREFILL_LARGE);
+    a.g_bn = (int32_t)gemm_bn(a.g_bm);
+    a.g_ks = (int32_t)gemm_ks(M, N, K, path == SPEAR_PATH_PREFILL_LARGE);
     a.L = L;
+    a.P.hdr = L.hdr;
+    a.P.zeros = L.zeros;
+    a.P.vhi = L.vhi;
+    a.P.vlo = L.vlo;
+    a.P.vtag = L.vtag;
+    a.P.active = L.active;
+    a.P.preu = L.preu;
+    a.P.prez = L.prez;
+    a.P.gpart = L.gpart;
+    a.P.idx = L.idx;
     // 32-bit copies for the decode kernels (checked on their paths; the
     // others read only hdr and epoch from here, at the start of the layout)
     a.D.hdr = (uint32_t)L.hdr;
@@ -509,8 +519,8 @@ static spear_status launch_path(LinearArgs &a, const spear_ec *ec, int32_t path,
             int64_t ks = cdiv(room, tg);
             const int64_t most = T / pw > 0 ? T / pw : 1;
             ks = ks < most ? ks : most;
-            a.pre_ks = ks;
-            a.npre = cdiv(tg * ks, 8) * 8;                // XCD-aligned start of the GEMM blocks
+            a.pre_ks = (int32_t)ks;
+            a.npre = (int32_t)(cdiv(tg * ks, 8) * 8);     // XCD-aligned start of the GEMM blocks
             e = launch_gemm(a, 2, 0, s);
             if (e == hipSuccess && (a.idx_out || a.nact_out))
                 e = launch_compact(active, M, a.idx_out, a.nact_out, s);

@@ -102,10 +102,10 @@ __device__ void prepass_finish(const LinearArgs &a, int64_t m0, const f32x4 (*s_
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, m = m0 + lr;
     const int rpad = a.rpad;
-    uint16_t *vhi = reinterpret_cast<uint16_t *>(a.ws + a.L.vhi);
-    uint16_t *vlo = reinterpret_cast<uint16_t *>(a.ws + a.L.vlo);
-    uint64_t *vtag = reinterpret_cast<uint64_t *>(a.ws + a.L.vtag);
-    int32_t *active = reinterpret_cast<int32_t *>(a.ws + a.L.active);
+    uint16_t *vhi = reinterpret_cast<uint16_t *>(a.ws + a.P.vhi);
+    uint16_t *vlo = reinterpret_cast<uint16_t *>(a.ws + a.P.vlo);
+    uint64_t *vtag = reinterpret_cast<uint64_t *>(a.ws + a.P.vtag);
+    int32_t *active = reinterpret_cast<int32_t *>(a.ws + a.P.active);
     if (tid < 16) {
         const double z = (double)a.b + s_zw[tid];
         const int64_t mm = m0 + tid;
@@ -267,8 +267,8 @@ __device__ __forceinline__ void prepass_tail(const LinearArgs &a, const int64_t 
     if (KS > 1) {
         // Tagged slice partials: [slot][tile][lane][4] words of u and [slot][token][2]
         // words of the fp64 logit, slot = group * pre_ks + slice.
-        uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.L.preu);
-        uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.L.prez);
+        uint64_t *pu = reinterpret_cast<uint64_t *>(a.ws + a.P.preu);
+        uint64_t *pz = reinterpret_cast<uint64_t *>(a.ws + a.P.prez);
         const int nel = ntile * 256;                      // u elements of a slot
         const float *uw = reinterpret_cast<const float *>(sh.uw);
         if (ks < KS - 1) {
@@ -370,7 +370,7 @@ __device__ __forceinline__ void prepass_tail(const LinearArgs &a, const int64_t 
         __syncthreads();
         bad = *sh.bad != 0;
         if (bad && tid == 0)          // an expired wait: counted; the group's v is NaN
-            atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+            atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.P.hdr) + HDR_TIMEOUTS, 1u);
     }
     prepass_finish(a, m0, sh.uw, sh.zw, sh.g, sh.act, sh.hid, tid, lane, wave, PW, tagged, tag,
                    bad);
@@ -387,10 +387,10 @@ __global__ __launch_bounds__(64 * PRE_WAVES) void prepass_kernel(const LinearArg
     __shared__ int s_act[16];
     __shared__ uint32_t s_tag, s_bad;
     __shared__ float s_hid[16 * SPEAR_MAX_GATE_HIDDEN];
-    pin_args(a);
+    pin_pre_args(a);
     uint64_t claimed = opaque_zero64();
     if (a.pre_ks > 1 && threadIdx.x == 0)
-        claimed = epoch_claim(a, gridDim.x);              // back long before it is used
+        claimed = epoch_claim(a, a.grid);              // back long before it is used
     const PreShared<PRE_WAVES> sh = {s_u, s_u + PRE_WAVES / 2, s_z, s_wg, s_uw, s_zw, s_g, s_act,
                                      &s_tag, &s_bad, s_hid};
     prepass_body<PRE_WAVES>(a, blockIdx.x, sh, claimed, false);
@@ -433,20 +433,20 @@ __global__ __launch_bounds__(512) void prepass2_kernel(const LinearArgs a)
     __shared__ uint32_t s_tag, s_bad;
     __shared__ float s_hid[16 * SPEAR_MAX_GATE_HIDDEN];
     uint8_t *const ring[RING] = {s_r0, s_r1, s_r2};
-    pin_args(a);
+    pin_pre_args(a);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
     const int64_t M = a.M, K = a.K, KS = a.pre_ks, r = a.r;
     uint64_t claimed = opaque_zero64();
     if (KS > 1 && tid == 0)
-        claimed = epoch_claim(a, gridDim.x);
+        claimed = epoch_claim(a, a.grid);
     const int64_t grp = blockIdx.x / KS, ks = blockIdx.x % KS;
     const int64_t m0 = grp * 16;
     const int64_t T = K / 32;
     const int64_t kb = 32 * (ks * T / KS), ke = 32 * ((ks + 1) * T / KS);   // this slice's depths
     const int64_t nch = (ke - kb + CK - 1) / CK;
-    const uint8_t *zsrc = a.ws + a.L.zeros + 16 * (lane & 15);
+    const uint8_t *zsrc = a.ws + a.P.zeros + 16 * (lane & 15);
 
     // DMA instruction i of this wave fills stage bytes (8 i + wave) KB + 16 lane:
     // row rho, swizzled position p, logical 16-byte chunk c of the row.
@@ -659,7 +659,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     uint8_t *const s_wb[6] = {s_w0, s_w1, s_w2, s_w3, s_w4, s_w5};
 
     __shared__ uint32_t s_tagg, s_tbad;
-    pin_args(a);
+    pin_pre_args(a);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar branches
 
@@ -668,7 +668,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     uint64_t claimed = opaque_zero64();
     if constexpr (EC == 2) {
         if (tid == 0)
-            claimed = epoch_claim(a, gridDim.x);
+            claimed = epoch_claim(a, a.grid);
         if ((int64_t)blockIdx.x < a.npre) {
             // u: waves 0 .. PW/2 - 1 in s_x0, the others in s_x1; the workgroup's u in
             // s_x2; logit partials and w_g in c0 (s_w0, or s_x3 when the
@@ -717,7 +717,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     const int64_t n0 = (tile % tiles_n) * G2_BN, m0 = (tile / tiles_n) * G2_BM;
     const int64_t S = (K + 127) / 128;
     const int64_t sb = ks * S / KS, se = (ks + 1) * S / KS;   // this slice's stages
-    const uint8_t *zsrc = a.ws + a.L.zeros + 16 * (lane & 15);
+    const uint8_t *zsrc = a.ws + a.P.zeros + 16 * (lane & 15);
 
     // DMA of one stage.  Activations: instruction j of wave w fills rows
     // 4 (G2_XI w + j) .. +3, lane i the slot i of that 1 KB (chunk (i % 16) ^
@@ -777,8 +777,8 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     // round trip overlaps the main loop (48 registers, which both tile shapes
     // have to spare).
     auto ec_load = [&](int t, u32x4 *vh, u32x4 *vl, u32x4 *bf) {
-        const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
-        const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
+        const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.P.vhi);
+        const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.P.vlo);
         const int rpad = a.rpad, r = a.r;
         const int j = 32 * t + 8 * lg;
 #pragma unroll
@@ -1058,7 +1058,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
         // tiles do not flood the memory system the pre-pass needs.  Bounded; an
         // expired wait makes the whole tile NaN (its EC term is unknown) and is
         // counted.
-        const uint64_t *vtag = reinterpret_cast<const uint64_t *>(a.ws + a.L.vtag);
+        const uint64_t *vtag = reinterpret_cast<const uint64_t *>(a.ws + a.P.vtag);
         const uint32_t tag = s_tagg;
         const int rpad = a.rpad, r = a.r;
         const int64_t nch = rpad / 32;
@@ -1127,7 +1127,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
             __syncthreads();
             if (s_tbad & (1u << (t & 31))) {
                 if (tid == 0)
-                    atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.L.hdr) + HDR_TIMEOUTS, 1u);
+                    atomicAdd(reinterpret_cast<uint32_t *>(a.ws + a.P.hdr) + HDR_TIMEOUTS, 1u);
                 const float qnan = __builtin_nanf("");
 #pragma unroll
                 for (int fn = 0; fn < G2_FN; fn++)
@@ -1170,7 +1170,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
     if (EC == 1 && ks < a.rpad / 32) {
         // Rank chunks of 32: slice ks takes chunks ks, ks + KS, ... (the
         // second launch adds the slices), so a K split also splits the EC.
-        const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
+        const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.P.active);
         int any = 0;
 #pragma unroll
         for (int fm = 0; fm < G2_FM; fm++) {
@@ -1206,7 +1206,7 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
         return;                                               // the column's first wave stores
     if (SPLIT) {
         // the scaled partial tile of this slice: unit-major, row-major bm x 256
-        float *part = reinterpret_cast<float *>(a.ws + a.L.gpart) + unit * (G2_BM * G2_BN);
+        float *part = reinterpret_cast<float *>(a.ws + a.P.gpart) + unit * (G2_BM * G2_BN);
 #pragma unroll
         for (int fm = 0; fm < G2_FM; fm++) {
             const int row = (wm * G2_FM + fm) * 16 + lr;
@@ -1268,7 +1268,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
     const int64_t tiles_n = (N + bn - 1) / bn, ntiles = tiles_n * ((M + bm - 1) / bm);
     const int64_t tile = (m / bm) * tiles_n + n / bn;
     const int64_t off = (m % bm) * bn + n % bn;
-    const f32x4 *part = reinterpret_cast<const f32x4 *>(a.ws + a.L.gpart);
+    const f32x4 *part = reinterpret_cast<const f32x4 *>(a.ws + a.P.gpart);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
         f32x4 p[CMB_U];
@@ -1313,9 +1313,10 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
     const dim3 block(64 * WN * WM * WK);
     // EC == 2: the pre-pass blocks come first in the grid
     const int64_t pre = EC == 2 ? a.npre : 0;
+    LinearArgs ka = a;
+    ka.grid = (uint32_t)(pre + ntiles * (a.g_ks > 1 ? a.g_ks : 1));   // read instead of gridDim
     if (a.g_ks > 1) {
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1, WK, FN, WN, KF>), dim3((unsigned)(pre + ntiles * a.g_ks)),
-                           block, 0, s, a);
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 1, EC, 1, WK, FN, WN, KF>), dim3(ka.grid), block, 0, s, ka);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
             return e;
@@ -1329,9 +1330,9 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
         return hipGetLastError();
     }
     if (a.out_f32)
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1, WK, FN, WN, KF>), dim3((unsigned)(pre + ntiles)), block, 0, s, a);
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 1, WK, FN, WN, KF>), dim3(ka.grid), block, 0, s, ka);
     else
-        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0, WK, FN, WN, KF>), dim3((unsigned)(pre + ntiles)), block, 0, s, a);
+        hipLaunchKernelGGL((gemm2_kernel<WM, FM, 0, EC, 0, WK, FN, WN, KF>), dim3(ka.grid), block, 0, s, ka);
     return hipGetLastError();
 }
 
@@ -1352,8 +1353,8 @@ __global__ __launch_bounds__(256) void ec_apply_kernel(const LinearArgs a)
     const int64_t M = a.M, N = a.N;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    const int32_t *list = reinterpret_cast<const int32_t *>(a.ws + a.L.idx);
-    const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.L.active);
+    const int32_t *list = reinterpret_cast<const int32_t *>(a.ws + a.P.idx);
+    const int32_t *active = reinterpret_cast<const int32_t *>(a.ws + a.P.active);
     const int32_t nact = list[a.mpad];
     const bool bad = nact < 0;
     const int64_t cnt = bad ? M : nact;
@@ -1367,8 +1368,8 @@ __global__ __launch_bounds__(256) void ec_apply_kernel(const LinearArgs a)
     const int flag = m >= 0 ? active[m] : 0;
     const bool use = m >= 0 && flag != 0;
     const int64_t n0 = (int64_t)blockIdx.y * 256 + 64 * wave;
-    const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.L.vhi);
-    const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.L.vlo);
+    const uint16_t *vhi = reinterpret_cast<const uint16_t *>(a.ws + a.P.vhi);
+    const uint16_t *vlo = reinterpret_cast<const uint16_t *>(a.ws + a.P.vlo);
     const int rpad = a.rpad, r = a.r;
     f32x4 acc[4];
 #pragma unroll
@@ -1418,12 +1419,14 @@ hipError_t launch_ec_apply(const LinearArgs &a, hipStream_t s)
 hipError_t launch_prepass(const LinearArgs &a, hipStream_t s)
 {
     const unsigned grid = (unsigned)((a.M + 15) / 16) * (unsigned)a.pre_ks;
+    LinearArgs ka = a;
+    ka.grid = grid;                                       // read instead of gridDim
     if (a.rpad == 32)
-        hipLaunchKernelGGL(prepass2_kernel<32>, dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL(prepass2_kernel<32>, dim3(grid), dim3(512), 0, s, ka);
     else if (a.rpad == 64)
-        hipLaunchKernelGGL(prepass2_kernel<64>, dim3(grid), dim3(512), 0, s, a);
+        hipLaunchKernelGGL(prepass2_kernel<64>, dim3(grid), dim3(512), 0, s, ka);
     else
-        hipLaunchKernelGGL(prepass_kernel, dim3(grid), dim3(64 * PRE_WAVES), 0, s, a);
+        hipLaunchKernelGGL(prepass_kernel, dim3(grid), dim3(64 * PRE_WAVES), 0, s, ka);
     return hipGetLastError();
 }
 

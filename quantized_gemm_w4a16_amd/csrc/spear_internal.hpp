@@ -178,18 +178,24 @@ struct LinearArgs {
     float alpha;
     DecOffsets D;
     uint32_t grid;   // decode: the launch's workgroups (gridDim lives in a line of its own)
-    // The rest: the vector gate MLP, the prefill tiling and the full layout.
+    // The prefill kernels load the leading block and this one (bytes 0 to 359,
+    // six lines): the vector gate MLP, the prefill tiling and the offsets of the
+    // workspace regions they use (64-bit: a prefill workspace may pass 4 GiB).
     const float *gw1, *gc1, *gw2, *gc2;   // vector gate MLP (gate_h > 0)
+    int32_t pre_ks;  // EC pre-pass: K slices per token group
+    int32_t g_bm;    // MFMA GEMM: tokens per tile (64 or 128)
+    int32_t g_bn;    // MFMA GEMM: channels per tile (64 with 64-token tiles, else 256)
+    int32_t g_ks;    // MFMA GEMM: K slices per tile (partials reduced by a second launch)
+    int32_t npre;    // K-split GEMM with the EC pre-pass in its launch: leading pre-pass blocks
     int64_t mpad;
-    int64_t pre_ks;  // EC pre-pass: K slices per token group
-    int64_t g_bm;    // MFMA GEMM: tokens per tile (64 or 128)
-    int64_t g_bn;    // MFMA GEMM: channels per tile (64 with 64-token tiles, else 256)
-    int64_t g_ks;    // MFMA GEMM: K slices per tile (partials reduced by a second launch)
-    int64_t npre;    // K-split GEMM with the EC pre-pass in its launch: leading pre-pass blocks
+    struct {
+        size_t hdr, zeros, vhi, vlo, vtag, active, preu, prez, gpart, idx;
+    } P;
+    // Host side only.
     WsLayout L;
 };
 static_assert(offsetof(LinearArgs, gw1) == 216 && offsetof(LinearArgs, D) == 180 &&
-                  offsetof(LinearArgs, grid) == 212,
+                  offsetof(LinearArgs, grid) == 212 && offsetof(LinearArgs, L) == 360,
               "the decode kernels' leading block");
 
 // Explicit counter waits (gfx9 s_waitcnt encoding: vmcnt bits 3:0 and 15:14,
@@ -204,9 +210,11 @@ __device__ __forceinline__ void wait_vmcnt()
 __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 __device__ __forceinline__ void bare_barrier() { __builtin_amdgcn_s_barrier(); }
 
-// Load every kernel argument at entry.  The compiler otherwise fetches fields
-// of a large argument struct lazily, in several batches that each cost a
-// memory round trip before the first data load can be issued.
+// Load the arguments a kernel uses at entry, in one batch.  The compiler
+// otherwise fetches fields of a large argument struct lazily, in several
+// batches that each cost a memory round trip before the first data load can
+// be issued; and each 64-byte line of arguments loaded costs about 0.35 us a
+// launch, so each kernel family loads only the leading lines it uses.
 template <typename T>
 __device__ __forceinline__ void pin_arg(const T &v)
 {
@@ -217,19 +225,6 @@ __device__ __forceinline__ void pin_arg(const T &v)
         asm volatile("" ::"s"(__builtin_bit_cast(uint32_t, v)));
 }
 
-__device__ __forceinline__ void pin_args(const LinearArgs &a)
-{
-    pin_arg(a.x); pin_arg(a.packed); pin_arg(a.scales); pin_arg(a.zeros); pin_arg(a.A);
-    pin_arg(a.B); pin_arg(a.wg); pin_arg(a.y); pin_arg(a.ws); pin_arg(a.g_out);
-    pin_arg(a.idx_out); pin_arg(a.nact_out); pin_arg(a.thr); pin_arg(a.b); pin_arg(a.hard);
-    pin_arg(a.r); pin_arg(a.rpad); pin_arg(a.M); pin_arg(a.N); pin_arg(a.K); pin_arg(a.ncg);
-    pin_arg(a.ksplit); pin_arg(a.spw); pin_arg(a.nprod); pin_arg(a.prod_k); pin_arg(a.mpad);
-    pin_arg(a.pre_ks); pin_arg(a.g_ks); pin_arg(a.g_bn); pin_arg(a.npre); pin_arg(a.L.vtag); pin_arg(a.L.gpart); pin_arg(a.L.preu); pin_arg(a.L.prez);
-    pin_arg(a.L.hdr); pin_arg(a.D.epoch); pin_arg(a.L.zeros); pin_arg(a.L.splitp); pin_arg(a.L.pu);
-    pin_arg(a.L.pz); pin_arg(a.L.vhi); pin_arg(a.L.vlo); pin_arg(a.L.active); pin_arg(a.L.idx);
-    pin_arg(a.wait_limit); pin_arg(a.out_f32);
-    pin_arg(a.gw1); pin_arg(a.gc1); pin_arg(a.gw2); pin_arg(a.gc2); pin_arg(a.gate_h); pin_arg(a.alpha);
-}
 
 // The decode kernels' arguments: the leading block only (the vector gate's
 // weights are loaded where that path needs them).
@@ -243,6 +238,17 @@ __device__ __forceinline__ void pin_dec_args(const LinearArgs &a)
     pin_arg(a.wait_limit); pin_arg(a.out_f32); pin_arg(a.gate_h); pin_arg(a.alpha);
     pin_arg(a.D.hdr); pin_arg(a.D.epoch); pin_arg(a.D.splitp); pin_arg(a.D.pu);
     pin_arg(a.D.pz); pin_arg(a.D.vhi); pin_arg(a.D.vlo); pin_arg(a.D.active); pin_arg(a.grid);
+}
+
+// The prefill kernels' arguments: the leading block and the prefill block.
+__device__ __forceinline__ void pin_pre_args(const LinearArgs &a)
+{
+    pin_dec_args(a);
+    pin_arg(a.gw1); pin_arg(a.gc1); pin_arg(a.gw2); pin_arg(a.gc2);
+    pin_arg(a.pre_ks); pin_arg(a.g_bm); pin_arg(a.g_bn); pin_arg(a.g_ks); pin_arg(a.npre);
+    pin_arg(a.mpad);
+    pin_arg(a.P.hdr); pin_arg(a.P.zeros); pin_arg(a.P.vhi); pin_arg(a.P.vlo); pin_arg(a.P.vtag);
+    pin_arg(a.P.active); pin_arg(a.P.preu); pin_arg(a.P.prez); pin_arg(a.P.gpart); pin_arg(a.P.idx);
 }
 
 // ---------------------------------------------- tagged cross-workgroup exchange
