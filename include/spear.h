@@ -213,6 +213,9 @@ spear_status spear_workspace_init(void *ws, size_t bytes, void *stream);
  * epilogue (ranks up to 32; larger ranks take the pre-pass form of the decode
  * path, two launches), or at the end of the EC pre-pass.
  * The result does not depend on the path beyond fp32 rounding order.
+ * SPEAR_E_SHAPE also when a decode path's workspace layout would place the
+ * regions its kernels use beyond 4 GiB (their offsets travel as 32-bit values;
+ * only layers with billions of channel groups times K ranges come near).
  */
 spear_status spear_w4_linear(const spear_bf16 *x, int64_t M, const spear_w4 *w,
                              const spear_ec *ec, void *y, int32_t out_dtype,
