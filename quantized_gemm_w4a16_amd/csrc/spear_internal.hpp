@@ -177,7 +177,7 @@ struct LinearArgs {
     int32_t gate_h;  // vector gate: hidden width (0: scalar gate only)
     float alpha;
     DecOffsets D;
-    uint32_t grid;   // decode: the launch's workgroups (gridDim lives in a line of its own)
+    uint32_t grid;   // the launch's workgroups (gridDim's hidden argument sits in a line of its own)
     // The prefill kernels load the leading block and this one (bytes 0 to 359,
     // six lines): the vector gate MLP, the prefill tiling and the offsets of the
     // workspace regions they use (64-bit: a prefill workspace may pass 4 GiB).
