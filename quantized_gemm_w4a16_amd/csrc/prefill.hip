@@ -1255,11 +1255,13 @@ __global__ __launch_bounds__(64 * G2_WN * G2_WM * G2_WK) void gemm2_kernel(const
 }
 
 // Second launch of a K-split GEMM: y = the sum of the slices' partial tiles in
-// slice order; a thread takes 4 consecutive channels of one token.
+// slice order; a thread takes 4 consecutive channels of one token.  Its few
+// values come as plain arguments (one 64-byte line; read from the layer's
+// argument block they would span five).
 template <int OUT_F32>
-__global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(void *yv, const uint8_t *partv, int64_t M,
+                                                            int64_t N, int32_t KS, int32_t bm, int32_t bn)
 {
-    const int64_t M = a.M, N = a.N, KS = a.g_ks, bm = a.g_bm, bn = a.g_bn;
     const int64_t nq = (N + 3) / 4;
     const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (idx >= M * nq)
@@ -1268,7 +1270,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
     const int64_t tiles_n = (N + bn - 1) / bn, ntiles = tiles_n * ((M + bm - 1) / bm);
     const int64_t tile = (m / bm) * tiles_n + n / bn;
     const int64_t off = (m % bm) * bn + n % bn;
-    const f32x4 *part = reinterpret_cast<const f32x4 *>(a.ws + a.P.gpart);
+    const f32x4 *part = reinterpret_cast<const f32x4 *>(partv);
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     for (int64_t q0 = 0; q0 < KS; q0 += CMB_U) {
         f32x4 p[CMB_U];
@@ -1282,7 +1284,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
                 v += p[i];
     }
     if (OUT_F32) {
-        float *y = reinterpret_cast<float *>(a.y) + m * N;
+        float *y = reinterpret_cast<float *>(yv) + m * N;
         if (n + 3 < N && (N & 3) == 0) {
             *reinterpret_cast<f32x4 *>(y + n) = v;
         } else {
@@ -1291,7 +1293,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const LinearArgs a)
                     y[n + i] = v[i];
         }
     } else {
-        uint16_t *y = reinterpret_cast<uint16_t *>(a.y) + m * N;
+        uint16_t *y = reinterpret_cast<uint16_t *>(yv) + m * N;
         if (n + 3 < N && (N & 3) == 0) {
             uint2 o;
             o.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
@@ -1321,12 +1323,13 @@ hipError_t launch_gemm2_t(const LinearArgs &a, hipStream_t s)
         if (e != hipSuccess)
             return e;
         const int64_t threads = a.M * ((a.N + 3) / 4);
+        const uint8_t *part = a.ws + a.P.gpart;
         if (a.out_f32)
             hipLaunchKernelGGL(splitk_reduce_kernel<1>, dim3((unsigned)((threads + 255) / 256)),
-                               dim3(256), 0, s, a);
+                               dim3(256), 0, s, a.y, part, a.M, a.N, a.g_ks, a.g_bm, a.g_bn);
         else
             hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3((unsigned)((threads + 255) / 256)),
-                               dim3(256), 0, s, a);
+                               dim3(256), 0, s, a.y, part, a.M, a.N, a.g_ks, a.g_bm, a.g_bn);
         return hipGetLastError();
     }
     if (a.out_f32)
